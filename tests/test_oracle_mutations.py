@@ -1,0 +1,146 @@
+"""Plant plausible mistakes in a private copy of the oracle; the pins must catch each (CPU)."""
+import importlib.util
+import math
+import os
+
+import numpy as np
+import pytest
+
+from tests import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "dsa_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("oracle_mutant", SRC)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def _indexer_row(relu=True, w_inside=False, mask_shift=0, drop_w=False):
+    def f(q_bt, w_bt, k_b, pos, Lmax):
+        out = np.full(Lmax, -np.inf)
+        n = int(min(pos + 1 + mask_shift, Lmax))
+        if n <= 0:
+            return out
+        dots = np.asarray(q_bt, np.float64) @ np.asarray(k_b[:n], np.float64).T
+        w = np.ones_like(w_bt) if drop_w else np.asarray(w_bt, np.float64)
+        if w_inside:
+            out[:n] = np.maximum(w[:, None] * dots, 0.0).sum(0)
+        else:
+            out[:n] = w @ (np.maximum(dots, 0.0) if relu else dots)
+        return out
+    return f
+
+
+def _e4m3(bias=7, sub_exp=-6):
+    def f(bits):
+        b = np.asarray(bits).astype(np.int64) & 0xFF
+        sign = np.where((b & 0x80) != 0, -1.0, 1.0)
+        e = (b >> 3) & 0xF
+        m = (b & 0x7).astype(np.float64)
+        mag = np.where(e == 0, (m / 8) * 2.0 ** sub_exp, (1 + m / 8) * np.exp2((e - bias).astype(float)))
+        return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+    return f
+
+
+def _topk(tie_high=False, descending=False, vis_shift=0):
+    def f(scores_row, n_visible, k):
+        n = int(max(0, min(n_visible + vis_shift, scores_row.shape[0])))
+        out = np.full(k, -1, dtype=np.int32)
+        if n == 0:
+            return out
+        s = np.asarray(scores_row[:n], np.float64)
+        pos = -np.arange(n) if tie_high else np.arange(n)
+        order = np.lexsort((pos, -s))
+        take = np.sort(order[:min(k, n)])
+        if descending:
+            take = take[::-1]
+        out[:take.shape[0]] = take
+        return out
+    return f
+
+
+def _attend(no_scale=False, no_max_in_lse=False, value_slice_end=False):
+    def f(q_h, rows, scale, d_v):
+        Hq = q_h.shape[0]
+        if rows.shape[0] == 0:
+            return np.zeros((Hq, d_v)), np.full(Hq, -np.inf)
+        logits = (1.0 if no_scale else scale) * (q_h @ rows.T)
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        z = p.sum(axis=1, keepdims=True)
+        vals = rows[:, -d_v:] if value_slice_end else rows[:, :d_v]
+        out = (p @ vals) / z
+        lse = np.log(z)[:, 0] if no_max_in_lse else (m + np.log(z))[:, 0]
+        return out, lse
+    return f
+
+
+def _sparse_attn_no_filter(o):
+    def f(q, kv, idx, ctx_len, scale, d_v, rows=None):
+        q = np.asarray(q, np.float64)
+        B, T, Hq, _ = q.shape
+        outs, lses = [], []
+        for b in range(B):
+            for t in range(T):
+                sel = np.asarray(idx[b, t], dtype=np.int64)
+                sel = sel[sel < kv.shape[1]]          # -1 now wraps to the last row
+                oo, ll = o._softmax_attend(q[b, t], kv[b, sel], scale, d_v)
+                outs.append(oo); lses.append(ll)
+        return np.stack(outs).reshape(B, T, Hq, d_v), np.stack(lses).reshape(B, T, Hq)
+    return f
+
+
+def _stack_reuse_first_f(o):
+    orig = o.run_stack
+
+    def f(pattern, layers, ctx_len, k, scale, d_v, attend=True):
+        res = orig(pattern, layers, ctx_len, k, scale, d_v, attend)
+        first = res["idx"][0]
+        res["idx"] = [first if c == "S" else i for c, i in zip(pattern, res["idx"])]
+        if attend:
+            res["out"] = [o.sparse_attn(layers[l]["q"], layers[l]["kv"], res["idx"][l], ctx_len,
+                                        scale, d_v)[0] for l in range(len(pattern))]
+        return res
+    return f
+
+
+MUTANTS = {
+    "indexer_no_relu": ("indexer_scores_row", lambda o: _indexer_row(relu=False)),
+    "indexer_w_inside_relu": ("indexer_scores_row", lambda o: _indexer_row(w_inside=True)),
+    "indexer_mask_off_by_one": ("indexer_scores_row", lambda o: _indexer_row(mask_shift=-1)),
+    "indexer_drops_w": ("indexer_scores_row", lambda o: _indexer_row(drop_w=True)),
+    "e4m3_bias_8": ("e4m3fn_bits_to_f64", lambda o: _e4m3(bias=8)),
+    "e4m3_subnormal_exp": ("e4m3fn_bits_to_f64", lambda o: _e4m3(sub_exp=-7)),
+    "topk_ties_to_higher_pos": ("topk_row", lambda o: _topk(tie_high=True)),
+    "topk_descending_output": ("topk_row", lambda o: _topk(descending=True)),
+    "topk_visible_off_by_one": ("topk_row", lambda o: _topk(vis_shift=-1)),
+    "attn_no_scale": ("_softmax_attend", lambda o: _attend(no_scale=True)),
+    "attn_lse_without_max": ("_softmax_attend", lambda o: _attend(no_max_in_lse=True)),
+    "attn_values_wrong_slice": ("_softmax_attend", lambda o: _attend(value_slice_end=True)),
+    "attn_padding_not_ignored": ("sparse_attn", _sparse_attn_no_filter),
+    "stack_reuses_first_f": ("run_stack", _stack_reuse_first_f),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches(name):
+    attr, make = MUTANTS[name]
+    o = fresh_oracle()
+    setattr(o, attr, make(o))
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutation {name} escaped every pin"
+
+
+def test_unmutated_copy_passes():
+    o = fresh_oracle()
+    for pin in P.ALL_PINS:
+        pin(o)
+    assert math.isfinite(1.0)
