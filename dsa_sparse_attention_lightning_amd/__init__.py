@@ -1,1 +1,184 @@
-"""MI355X-native IndexCache / DeepSeek-Sparse-Attention hot path (placeholder; binding lands with the HIP library)."""
+"""MI355X-native IndexCache / DeepSeek-Sparse-Attention hot path.
+
+Thin Python binding over libdsa_indexcache.so (C ABI in include/dsa_indexcache.h):
+argument marshalling only - every step runs in the gfx950 HIP kernels.  Tensors
+must be contiguous device tensors; work is enqueued on torch's current stream.
+
+    indexer_scores(q, w, k, ctx_len, q_scale=None, k_scale=None) -> scores [B,T,Lmax]
+    topk(scores, ctx_len, k)                                     -> idx [B,T,k] int32
+    sparse_attn(q, kv, idx, ctx_len, scale)                      -> (out, lse)
+    run_stack(pattern, layers, ...)                              -> stats dict
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+from . import _lib
+from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
+
+__all__ = ["indexer_scores", "topk", "sparse_attn", "run_stack", "DSAError", "library",
+           "ld_for"]
+
+
+def library():
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise TypeError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def ld_for(Lmax: int) -> int:
+    return (Lmax + 3) // 4 * 4
+
+
+def _idx_dtype(q):
+    torch = _torch()
+    if q.dtype == torch.bfloat16:
+        return _lib.DSA_BF16
+    if q.dtype == torch.float8_e4m3fn:
+        return _lib.DSA_FP8_E4M3
+    raise TypeError(f"indexer inputs must be bf16 or float8_e4m3fn, got {q.dtype}")
+
+
+def indexer_scores(q, w, k, ctx_len, q_scale=None, k_scale=None, out=None, stream=None):
+    """Lightning-indexer scores [B,T,Lmax] fp32 (a view of a [B,T,ld] buffer)."""
+    torch = _torch()
+    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), 4)
+    _need(k, "k", (q.dtype,), 3)
+    _need(w, "w", (torch.float32,), 3)
+    _need(ctx_len, "ctx_len", (torch.int32,), 1)
+    B, T, H, D = q.shape
+    Lmax = k.shape[1]
+    ld = ld_for(Lmax)
+    if out is None:
+        out = torch.empty((B, T, ld), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    lib = library()
+    _lib.check(lib.dsa_indexer_scores(_ptr(q), _idx_dtype(q), _ptr(q_scale), _ptr(w), _ptr(k),
+                                      _ptr(k_scale), _ptr(ctx_len), B, T, H, D, Lmax,
+                                      _ptr(out), out.shape[-1], _stream(stream)))
+    return out[..., :Lmax]
+
+
+def topk(scores, ctx_len, k: int, out=None, stream=None):
+    """Per-row top-k positions, ascending, -1 padded: [B,T,k] int32.
+
+    `scores` may be the [B,T,Lmax] view returned by indexer_scores (its row
+    stride is then the padded buffer's)."""
+    torch = _torch()
+    if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise TypeError("scores must be a [B,T,L] float32 device tensor")
+    if scores.stride(2) != 1 or scores.stride(0) != scores.shape[1] * scores.stride(1):
+        raise TypeError("scores rows must be contiguous with a uniform row stride")
+    _need(ctx_len, "ctx_len", (torch.int32,), 1)
+    B, T, Lmax = scores.shape
+    ld = scores.stride(1)
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+    _need(out, "out", (torch.int32,), 3)
+    lib = library()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.dsa_topk_workspace_size(B, T, Lmax, k, ctypes.byref(need)))
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=scores.device)
+    _lib.check(lib.dsa_topk(_ptr(scores), ld, _ptr(ctx_len), B, T, Lmax, k, _ptr(out),
+                            _ptr(ws), need.value, _stream(stream)))
+    return out
+
+
+def sparse_attn(q, kv, idx, ctx_len, scale: float, out=None, lse=None, want_lse=True,
+                stream=None):
+    """Sparse MLA attention: (out [B,T,Hq,512] bf16, lse [B,T,Hq] fp32 or None)."""
+    torch = _torch()
+    _need(q, "q", (torch.bfloat16,), 4)
+    _need(kv, "kv", (torch.bfloat16,), 3)
+    _need(idx, "idx", (torch.int32,), 3)
+    _need(ctx_len, "ctx_len", (torch.int32,), 1)
+    B, T, Hq, d_qk = q.shape
+    Lmax = kv.shape[1]
+    k = idx.shape[2]
+    d_v = 512
+    if out is None:
+        out = torch.empty((B, T, Hq, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    lib = library()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.dsa_sparse_attn_workspace_size(B, T, Hq, k, d_v, ctypes.byref(need)))
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(idx), _ptr(ctx_len), B, T, Hq, Lmax,
+                                   k, d_qk, d_v, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                   need.value, _stream(stream)))
+    return out, lse
+
+
+class Stack:
+    """Pre-marshalled arguments of indexcache_run_stack for repeated calls."""
+
+    def __init__(self, pattern: str, layers: Sequence[Dict], ctx_len, *, B, T, H, D, Lmax, k,
+                 Hq=0, idx_dtype="bf16", scale=1.0, d_qk=576, d_v=512, device=None):
+        torch = _torch()
+        self.pattern = pattern.encode()
+        self.n_layers = len(layers)
+        self._keep = [layers, ctx_len]
+        arr = (Layer * self.n_layers)()
+        for i, L in enumerate(layers):
+            arr[i] = Layer(_ptr(L.get("q_idx")), _ptr(L.get("q_idx_scale")), _ptr(L.get("w")),
+                           _ptr(L.get("k_idx")), _ptr(L.get("k_idx_scale")), _ptr(L.get("q")),
+                           _ptr(L.get("kv")), _ptr(L.get("out")), _ptr(L.get("lse")))
+        self.layers = arr
+        dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
+        self.shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale))
+        self.ctx_len = ctx_len
+        dev = device if device is not None else ctx_len.device
+        self.ld = ld_for(Lmax)
+        self.idx_buf = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+        self.score_buf = torch.empty((B, T, self.ld), dtype=torch.float32, device=dev)
+        need = ctypes.c_size_t(0)
+        _lib.check(library().indexcache_stack_workspace_size(ctypes.byref(self.shape),
+                                                             ctypes.byref(need)))
+        self.ws_bytes = need.value
+        self.ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        self.stats = StackStats()
+
+    def run(self, stream=None) -> Dict[str, int]:
+        _lib.check(library().indexcache_run_stack(
+            self.pattern, self.n_layers, self.layers, ctypes.byref(self.shape),
+            _ptr(self.ctx_len), _ptr(self.idx_buf), _ptr(self.score_buf), self.ld, _ptr(self.ws),
+            self.ws_bytes, ctypes.byref(self.stats), _stream(stream)))
+        return dict(n_indexer_calls=self.stats.n_indexer_calls,
+                    n_topk_calls=self.stats.n_topk_calls, n_attn_calls=self.stats.n_attn_calls)
+
+
+def run_stack(pattern: str, layers: List[Dict], ctx_len, **shape) -> Dict:
+    """One pass of the IndexCache layer loop; returns stats plus idx_buf."""
+    st = Stack(pattern, layers, ctx_len, **shape)
+    stats = st.run()
+    stats["idx_buf"] = st.idx_buf
+    return stats

@@ -1,0 +1,308 @@
+// C ABI of the IndexCache / DSA hot path: host-side validation, dispatch to
+// the gfx950 kernels and the F/S layer-stack driver.
+//
+// The layer loop follows the IndexCache paper summary (technical §2 on the
+// gist.science es/pt/it/de editions): F layers run indexer + top-k and store
+// the index set in the one index buffer, S layers run neither and attend with
+// the buffer as the nearest preceding F layer left it.  The branch is taken
+// on the host from the pattern string; nothing is copied for S layers.
+#include "../../include/dsa_indexcache.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launchers.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status_t ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+dsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define CHECK_PTR(p)                                                                   \
+  do {                                                                                 \
+    if ((p) == nullptr) return fail(DSA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);   \
+    if (!aligned16(p))                                                                 \
+      return fail(DSA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p);      \
+  } while (0)
+
+#define CHECK(cond, st, ...)                          \
+  do {                                                \
+    if (!(cond)) return fail((st), __VA_ARGS__);      \
+  } while (0)
+
+constexpr int kMaxTopk = 16384;
+constexpr int kMaxAttnK = 65536;
+
+dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
+                           const float* q_scale, const float* w, const void* k,
+                           const float* k_scale, const int32_t* ctx_len, int B, int T, int H,
+                           int D, int Lmax, const float* scores, int64_t ld) {
+  CHECK(dtype == DSA_BF16 || dtype == DSA_FP8_E4M3, DSA_ERR_INVALID_ARG, "%s: unknown dtype %d",
+        fn, (int)dtype);
+  CHECK(B >= 1 && T >= 1 && Lmax >= 1, DSA_ERR_INVALID_ARG,
+        "%s: need B, T, Lmax >= 1 (got %d, %d, %d)", fn, B, T, Lmax);
+  CHECK(T <= Lmax, DSA_ERR_INVALID_ARG, "%s: T (%d) exceeds Lmax (%d)", fn, T, Lmax);
+  CHECK((int64_t)B * T <= 65535, DSA_ERR_UNSUPPORTED, "%s: B*T (%lld) above 65535", fn,
+        (long long)B * T);
+  CHECK(D == 64 || D == 128, DSA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+  CHECK(H >= 1 && H <= 64, DSA_ERR_UNSUPPORTED, "%s: H must be in 1..64 (got %d)", fn, H);
+  CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
+        "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
+        Lmax);
+  CHECK_PTR(q);
+  CHECK_PTR(w);
+  CHECK_PTR(k);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(scores);
+  if (dtype == DSA_FP8_E4M3) {
+    CHECK(q_scale != nullptr && k_scale != nullptr, DSA_ERR_INVALID_ARG,
+          "%s: fp8 inputs need q_scale and k_scale", fn);
+    CHECK_PTR(q_scale);
+    CHECK_PTR(k_scale);
+  } else {
+    CHECK(q_scale == nullptr && k_scale == nullptr, DSA_ERR_INVALID_ARG,
+          "%s: bf16 inputs take no scales", fn);
+  }
+  return DSA_OK;
+}
+
+dsa_status_t check_topk(const char* fn, const float* scores, int64_t ld, const int32_t* ctx_len,
+                        int B, int T, int Lmax, int k, const int32_t* idx) {
+  CHECK(B >= 1 && T >= 1 && Lmax >= 1, DSA_ERR_INVALID_ARG,
+        "%s: need B, T, Lmax >= 1 (got %d, %d, %d)", fn, B, T, Lmax);
+  CHECK(T <= Lmax, DSA_ERR_INVALID_ARG, "%s: T (%d) exceeds Lmax (%d)", fn, T, Lmax);
+  CHECK(k >= 1, DSA_ERR_INVALID_ARG, "%s: k must be >= 1 (got %d)", fn, k);
+  CHECK(k <= kMaxTopk, DSA_ERR_UNSUPPORTED, "%s: k (%d) above %d", fn, k, kMaxTopk);
+  CHECK((int64_t)B * T <= 2147483647LL / 2, DSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
+        "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
+        Lmax);
+  CHECK_PTR(scores);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(idx);
+  return DSA_OK;
+}
+
+dsa_status_t check_attn(const char* fn, const void* q, const void* kv, const int32_t* idx,
+                        const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k, int d_qk,
+                        int d_v, float scale, const void* out, const float* lse) {
+  CHECK(B >= 1 && T >= 1 && Lmax >= 1, DSA_ERR_INVALID_ARG,
+        "%s: need B, T, Lmax >= 1 (got %d, %d, %d)", fn, B, T, Lmax);
+  CHECK(T <= Lmax, DSA_ERR_INVALID_ARG, "%s: T (%d) exceeds Lmax (%d)", fn, T, Lmax);
+  CHECK(d_qk == 576 && d_v == 512, DSA_ERR_UNSUPPORTED,
+        "%s: only d_qk = 576, d_v = 512 is built (got %d, %d)", fn, d_qk, d_v);
+  CHECK(Hq >= 16 && Hq % 16 == 0 && Hq <= 1024, DSA_ERR_UNSUPPORTED,
+        "%s: Hq must be a multiple of 16 in 16..1024 (got %d)", fn, Hq);
+  CHECK(k >= 1 && k <= kMaxAttnK, DSA_ERR_UNSUPPORTED, "%s: k must be in 1..%d (got %d)", fn,
+        kMaxAttnK, k);
+  CHECK((int64_t)B * T <= 2147483647LL / 2, DSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  CHECK(scale > 0.f && scale == scale, DSA_ERR_INVALID_ARG, "%s: scale must be > 0", fn);
+  CHECK_PTR(q);
+  CHECK_PTR(kv);
+  CHECK_PTR(idx);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(out);
+  if (lse != nullptr) CHECK_PTR(lse);
+  return DSA_OK;
+}
+
+dsa_status_t run_indexer(const void* q, dsa_dtype_t dtype, const float* q_scale, const float* w,
+                         const void* k, const float* k_scale, const int32_t* ctx_len, int B,
+                         int T, int H, int D, int Lmax, float* scores, int64_t ld,
+                         hipStream_t stream) {
+  const bool fp8 = dtype == DSA_FP8_E4M3;
+  hipError_t e;
+  if (T > 1 && dsa::indexer_prefill_supported(H, D))
+    e = dsa::launch_indexer_prefill(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax,
+                                    scores, ld, stream);
+  else
+    e = dsa::launch_indexer_decode(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax,
+                                   scores, ld, stream);
+  return hip_status(e, "indexer launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* dsa_version(void) { return "0.1.0 gfx950"; }
+
+dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t dtype, const float* q_scale,
+                                const float* w, const void* k, const float* k_scale,
+                                const int32_t* ctx_len, int B, int T, int H, int D, int Lmax,
+                                float* scores, int64_t ld_scores, hipStream_t stream) {
+  const char* fn = "dsa_indexer_scores";
+  dsa_status_t st = check_indexer(fn, q, dtype, q_scale, w, k, k_scale, ctx_len, B, T, H, D,
+                                  Lmax, scores, ld_scores);
+  if (st != DSA_OK) return st;
+  return run_indexer(q, dtype, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax, scores,
+                     ld_scores, stream);
+}
+
+dsa_status_t dsa_topk_workspace_size(int B, int T, int Lmax, int k, size_t* bytes) {
+  const char* fn = "dsa_topk_workspace_size";
+  CHECK(bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  CHECK(B >= 1 && T >= 1 && Lmax >= 1 && k >= 1, DSA_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  *bytes = dsa::topk_workspace_bytes(B, T, Lmax, k);
+  return ok();
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx_len, int B,
+                      int T, int Lmax, int k, int32_t* idx, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_topk";
+  dsa_status_t st = check_topk(fn, scores, ld_scores, ctx_len, B, T, Lmax, k, idx);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa::topk_workspace_bytes(B, T, Lmax, k);
+  CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
+        "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+  if (need) CHECK_PTR(workspace);
+  return hip_status(dsa::launch_topk(scores, ld_scores, ctx_len, B, T, Lmax, k, idx, workspace,
+                                     workspace_bytes, stream),
+                    "topk launch");
+}
+
+dsa_status_t dsa_sparse_attn_workspace_size(int B, int T, int Hq, int k, int d_v,
+                                            size_t* bytes) {
+  const char* fn = "dsa_sparse_attn_workspace_size";
+  CHECK(bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  CHECK(B >= 1 && T >= 1 && Hq >= 16 && Hq % 16 == 0 && k >= 1 && d_v == 512,
+        DSA_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  *bytes = dsa::sparse_attn_workspace_bytes(B, T, Hq, k, d_v);
+  return ok();
+}
+
+dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
+                             const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k,
+                             int d_qk, int d_v, float scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dsa_sparse_attn";
+  dsa_status_t st =
+      check_attn(fn, q, kv, idx, ctx_len, B, T, Hq, Lmax, k, d_qk, d_v, scale, out, lse);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa::sparse_attn_workspace_bytes(B, T, Hq, k, d_v);
+  CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
+        "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+  if (need) CHECK_PTR(workspace);
+  return hip_status(dsa::launch_sparse_attn(q, kv, idx, ctx_len, B, T, Hq, Lmax, k, scale, out,
+                                            lse, workspace, workspace_bytes, stream),
+                    "sparse attention launch");
+}
+
+dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* s, size_t* bytes) {
+  const char* fn = "indexcache_stack_workspace_size";
+  CHECK(s != nullptr && bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: NULL argument", fn);
+  CHECK(s->B >= 1 && s->T >= 1 && s->Lmax >= 1 && s->k >= 1, DSA_ERR_INVALID_ARG,
+        "%s: bad sizes", fn);
+  size_t need = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
+  if (s->Hq > 0) {
+    CHECK(s->Hq % 16 == 0 && s->d_v == 512, DSA_ERR_INVALID_ARG, "%s: bad attention sizes", fn);
+    const size_t a = dsa::sparse_attn_workspace_bytes(s->B, s->T, s->Hq, s->k, s->d_v);
+    if (a > need) need = a;
+  }
+  *bytes = need;
+  return ok();
+}
+
+dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_layer_t* layers,
+                                  const dsa_stack_shape_t* shape, const int32_t* ctx_len,
+                                  int32_t* idx_buf, float* score_buf, int64_t ld_scores,
+                                  void* workspace, size_t workspace_bytes,
+                                  dsa_stack_stats_t* stats, hipStream_t stream) {
+  const char* fn = "indexcache_run_stack";
+  CHECK(pattern != nullptr && layers != nullptr && shape != nullptr, DSA_ERR_INVALID_ARG,
+        "%s: pattern, layers and shape must be non-NULL", fn);
+  CHECK(n_layers >= 1, DSA_ERR_INVALID_ARG, "%s: n_layers must be >= 1", fn);
+  const size_t plen = strnlen(pattern, (size_t)n_layers + 1);
+  CHECK(plen == (size_t)n_layers, DSA_ERR_INVALID_ARG,
+        "%s: pattern length %zu does not match n_layers %d", fn, plen, n_layers);
+  for (int l = 0; l < n_layers; ++l)
+    CHECK(pattern[l] == 'F' || pattern[l] == 'S', DSA_ERR_INVALID_ARG,
+          "%s: pattern[%d] = '%c' is neither 'F' nor 'S'", fn, l, pattern[l]);
+  CHECK(pattern[0] == 'F', DSA_ERR_INVALID_ARG,
+        "%s: pattern must start with 'F' (an S layer reuses the nearest preceding F)", fn);
+  const dsa_stack_shape_t& s = *shape;
+  CHECK(s.Hq >= 0, DSA_ERR_INVALID_ARG, "%s: Hq must be >= 0", fn);
+  size_t need = 0;
+  {
+    dsa_status_t st = indexcache_stack_workspace_size(shape, &need);
+    if (st != DSA_OK) return st;
+  }
+  CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
+        "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+  // Validate every layer before launching anything.
+  char what[96];
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    snprintf(what, sizeof(what), "%s (layer %d)", fn, l);
+    if (pattern[l] == 'F') {
+      dsa_status_t st = check_indexer(what, L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
+                                      L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
+                                      score_buf, ld_scores);
+      if (st != DSA_OK) return st;
+      st = check_topk(what, score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k, idx_buf);
+      if (st != DSA_OK) return st;
+    }
+    if (s.Hq > 0) {
+      dsa_status_t st = check_attn(what, L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax,
+                                   s.k, s.d_qk, s.d_v, s.scale, L.out, L.lse);
+      if (st != DSA_OK) return st;
+    }
+  }
+  dsa_stack_stats_t st_local = {0, 0, 0};
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    if (pattern[l] == 'F') {  // Full layer: fresh index set into the cache
+      dsa_status_t st = run_indexer(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
+                                    L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
+                                    score_buf, ld_scores, stream);
+      if (st != DSA_OK) return st;
+      st_local.n_indexer_calls++;
+      st = hip_status(dsa::launch_topk(score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k,
+                                       idx_buf, workspace, workspace_bytes, stream),
+                      "topk launch");
+      if (st != DSA_OK) return st;
+      st_local.n_topk_calls++;
+    }
+    // Shared layer: idx_buf already holds the nearest preceding F layer's set.
+    if (s.Hq > 0) {
+      dsa_status_t st = hip_status(
+          dsa::launch_sparse_attn(L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax, s.k,
+                                  s.scale, L.out, L.lse, workspace, workspace_bytes, stream),
+          "sparse attention launch");
+      if (st != DSA_OK) return st;
+      st_local.n_attn_calls++;
+    }
+  }
+  if (stats) *stats = st_local;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// MFMA wrappers, order-preserving float keys and block-wide scans.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MFMA
+// 32x32 output tiles: lane l holds column (l & 31) and rows
+// 8*(r/4) + 4*(l/32) + (r%4) for accumulator register r in 0..15.
+// Operand A: lane l holds row (l & 31); operand B: column (l & 31); the
+// reduction index inside a lane follows the same order for A and B, so any
+// consistent assignment of reduction indices to (lane/32, element) works.
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// fp8 e4m3 x fp8 e4m3, 64-deep reduction, unit block scales (E8M0 127 = 1.0).
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// 16x16 output tiles: lane l holds column (l & 15), rows 4*(l/16) + r.
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ i32x4 ld16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ i32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  // round to nearest even (inputs are finite)
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- keys
+// Order-preserving map float -> uint32: a > b (as floats, -0 == +0) iff
+// key(a) > key(b).  -0 is folded onto +0 so equal values get equal keys.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- scans
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Block-wide exclusive prefix sum of one value per thread.  `scratch` holds
+// NW words of LDS.  Returns the exclusive prefix; `total` gets the sum.
+// Contains two __syncthreads, so every thread of the block must call it.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch,
+                                                    uint32_t& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  uint32_t incl = wave_incl_scan(v);
+  if (lane == kWave - 1) scratch[wid] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    uint32_t t = scratch[i];
+    before += (i < wid) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
+}  // namespace dsa

@@ -1,0 +1,215 @@
+// Lightning-indexer scores for a prefill chunk (T > 1 query rows).
+//
+// Same score as the decode kernel (IndexCache paper summary, technical §1:
+// the indexer scores every previous token; DSA form
+// sum_h w * ReLU(q_h . k)), but here many queries share each key, so the
+// problem is a dense [T*H x D] . [D x L] contraction - 2*H*D flops per
+// (query, key) pair against a few bytes - and runs at MFMA speed:
+//
+//   * a workgroup holds 8 queries, one per wave; a wave keeps its query's
+//     [64 heads x D] block in registers (operand A of 32x32 MFMAs);
+//   * key tiles of 128 rows are staged through LDS (double-buffered, rows
+//     padded by 16 bytes so the 32 lanes of a fragment read hit distinct
+//     banks) and shared by the 8 waves: operand B, 32 keys per MFMA column
+//     block;
+//   * the fused epilogue (ReLU, head weight w' = w (bf16) or w * q_scale
+//     (fp8), sum over heads, key scale, causal mask) runs on the fp32
+//     accumulators, so only the final fp32 score reaches HBM;
+//   * causality: a workgroup never computes keys beyond its last query's
+//     position; those columns, and columns past each query's own position,
+//     are written as -inf.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace dsa {
+namespace {
+
+constexpr int kPfWaves = 8;    // queries per workgroup
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfTile = 128;   // keys per LDS tile
+
+template <bool FP8, int D, int HB>
+__global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
+    int Lmax, float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int ROWB = D * EB;          // bytes per key row
+  constexpr int PITCH = ROWB + 16;      // LDS row pitch
+  constexpr int HALF = ROWB / 2;        // bytes of a row per lane
+  constexpr int NV = HALF / 16;         // 16-byte vectors per lane per key
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  constexpr int CH = kPfTile * CPR / kPfThreads;  // staged chunks per thread
+  static_assert(CH >= 1 && kPfTile * CPR % kPfThreads == 0, "tile staging");
+  __shared__ __align__(16) uint8_t ks[2][kPfTile * PITCH];
+  __shared__ float kss[2][kPfTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int g = lane >> 5;
+  const int col = lane & 31;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.x * kPfWaves;
+  const int t = t0 + wave;
+  const bool live = t < T;
+  const int tq = min(t, T - 1);
+  const int64_t row = (int64_t)b * T + tq;
+  const int ctx = ctx_len[b];
+  const int64_t pos = (int64_t)ctx - T + t;
+  const int64_t pos_max = (int64_t)ctx - T + min(T - 1, t0 + kPfWaves - 1);
+  const int k0 = blockIdx.y * keys_per_wg;
+  const int k1 = min(Lmax, k0 + keys_per_wg);
+  const int kc = (int)max((int64_t)k0, min((int64_t)k1, pos_max + 1));  // computed: [k0, kc)
+  float* srow = scores + row * ld;
+
+  if (live)
+    for (int s = kc + lane; s < k1; s += kWave) srow[s] = -INFINITY;
+  if (kc <= k0) return;  // uniform over the workgroup
+
+  // Query fragments and head weights (zero for padded heads / idle waves).
+  i32x4 qv[HB][NV];
+  float wv[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = hb * 32 + col;
+    const uint8_t* qp = q + (row * H + head) * ROWB + g * HALF;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) qv[hb][v] = (head < H) ? ld16(qp + 16 * v) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      float wt = 0.f;
+      if (h < H && live) {
+        wt = w[row * H + h];
+        if (FP8) wt *= q_scale[row * H + h];
+      }
+      wv[hb][r] = wt;
+    }
+  }
+
+  const uint8_t* kb = k + (int64_t)b * Lmax * ROWB;
+  const float* ksb = FP8 ? k_scale + (int64_t)b * Lmax : nullptr;
+  const int ntiles = (kc - k0 + kPfTile - 1) / kPfTile;
+
+  i32x4 stage[CH];
+  float stage_s = 1.f;
+  auto gload = [&](int tile) {
+    const int base = k0 + tile * kPfTile;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * kPfThreads;
+      const int key = min(base + chunk / CPR, Lmax - 1);
+      stage[c] = ld16(kb + (int64_t)key * ROWB + (chunk % CPR) * 16);
+    }
+    if (FP8 && tid < kPfTile) stage_s = ksb[min(base + tid, Lmax - 1)];
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int chunk = tid + c * kPfThreads;
+      *reinterpret_cast<i32x4*>(&ks[buf][(chunk / CPR) * PITCH + (chunk % CPR) * 16]) = stage[c];
+    }
+    if (FP8 && tid < kPfTile) kss[buf][tid] = stage_s;
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < ntiles) gload(tile + 1);
+    const int tbase = k0 + tile * kPfTile;
+#pragma unroll
+    for (int sb = 0; sb < kPfTile / 32; ++sb) {
+      const int kbase = tbase + sb * 32;
+      if (kbase >= kc) break;
+      const uint8_t* bp = &ks[buf][(sb * 32 + col) * PITCH + g * HALF];
+      i32x4 bv[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) bv[v] = *reinterpret_cast<const i32x4*>(bp + 16 * v);
+      f32x16 acc[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16{};
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int s = 0; s < NV; ++s)
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+            acc[hb] = mfma32_bf16(as_bf16x8(qv[hb][s]), as_bf16x8(bv[s]), acc[hb]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < NV / 2; ++s) {
+          const i32x8 bk = {bv[2 * s][0], bv[2 * s][1], bv[2 * s][2], bv[2 * s][3],
+                            bv[2 * s + 1][0], bv[2 * s + 1][1], bv[2 * s + 1][2],
+                            bv[2 * s + 1][3]};
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            const i32x8 aq = {qv[hb][2 * s][0], qv[hb][2 * s][1], qv[hb][2 * s][2],
+                              qv[hb][2 * s][3], qv[hb][2 * s + 1][0], qv[hb][2 * s + 1][1],
+                              qv[hb][2 * s + 1][2], qv[hb][2 * s + 1][3]};
+            acc[hb] = mfma32_fp8(aq, bk, acc[hb]);
+          }
+        }
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc = fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), sc);
+      sc += __shfl_xor(sc, 32, kWave);
+      const int key = kbase + col;
+      if (g == 0 && live && key < kc) {
+        float o = -INFINITY;
+        if (key <= pos) o = FP8 ? sc * kss[buf][sb * 32 + col] : sc;
+        srow[key] = o;
+      }
+    }
+    if (tile + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+template <bool FP8, int D, int HB>
+hipError_t launch_pf(const void* q, const float* q_scale, const float* w, const void* k,
+                     const float* k_scale, const int32_t* ctx_len, int B, int T, int H, int Lmax,
+                     float* scores, int64_t ld, hipStream_t stream) {
+  const int qgroups = (T + kPfWaves - 1) / kPfWaves;
+  const int tiles = (Lmax + kPfTile - 1) / kPfTile;
+  // Split the keys so the grid holds >= ~8 workgroups per CU.
+  int splits = (2048 + qgroups * B - 1) / (qgroups * B);
+  splits = max(splits, 8);
+  splits = max(1, min(splits, tiles));
+  const int tiles_per = (tiles + splits - 1) / splits;
+  const int keys_per_wg = tiles_per * kPfTile;
+  const dim3 grid(qgroups, (Lmax + keys_per_wg - 1) / keys_per_wg, B);
+  hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D, HB>), grid, dim3(kPfThreads), 0, stream,
+                     (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, ctx_len, T, H,
+                     Lmax, scores, ld, keys_per_wg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_prefill_supported(int H, int D) { return H >= 1 && H <= 64 && (D == 64 || D == 128); }
+
+hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale, const float* w,
+                                  const void* k, const float* k_scale, const int32_t* ctx_len,
+                                  int B, int T, int H, int D, int Lmax, float* scores,
+                                  int64_t ld, hipStream_t stream) {
+#define DSA_PF(F8, DD, HBB) \
+  return launch_pf<F8, DD, HBB>(q, q_scale, w, k, k_scale, ctx_len, B, T, H, Lmax, scores, ld, stream)
+  const bool two = H > 32;
+  if (D == 128) {
+    if (fp8) { if (two) DSA_PF(true, 128, 2); DSA_PF(true, 128, 1); }
+    if (two) DSA_PF(false, 128, 2);
+    DSA_PF(false, 128, 1);
+  }
+  if (fp8) { if (two) DSA_PF(true, 64, 2); DSA_PF(true, 64, 1); }
+  if (two) DSA_PF(false, 64, 2);
+  DSA_PF(false, 64, 1);
+#undef DSA_PF
+}
+
+}  // namespace dsa

@@ -1,0 +1,36 @@
+// Host-side launchers of the gfx950 kernels.  Shapes are validated by the
+// C ABI layer before these are called; they only pick a launch
+// configuration and enqueue work on the stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Indexer scores, one query row at a time, keys streamed from HBM (T == 1
+// decode, and the row-wise fallback for prefill).
+hipError_t launch_indexer_decode(const void* q, bool fp8, const float* q_scale, const float* w,
+                                 const void* k, const float* k_scale, const int32_t* ctx_len,
+                                 int B, int T, int H, int D, int Lmax, float* scores,
+                                 int64_t ld, hipStream_t stream);
+
+// Indexer scores for a prefill chunk (T > 1): MFMA tiles over (query, key).
+hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale, const float* w,
+                                  const void* k, const float* k_scale, const int32_t* ctx_len,
+                                  int B, int T, int H, int D, int Lmax, float* scores,
+                                  int64_t ld, hipStream_t stream);
+bool indexer_prefill_supported(int H, int D);
+
+size_t topk_workspace_bytes(int B, int T, int Lmax, int k);
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, int B, int T,
+                       int Lmax, int k, int32_t* idx, void* workspace, size_t ws_bytes,
+                       hipStream_t stream);
+
+size_t sparse_attn_workspace_bytes(int B, int T, int Hq, int k, int d_v);
+hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
+                              const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k,
+                              float scale, void* out, float* lse, void* workspace,
+                              size_t ws_bytes, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,179 @@
+/*
+ * dsa_indexcache.h - C ABI of the MI355X (gfx950) IndexCache / DeepSeek
+ * Sparse Attention hot path.
+ *
+ * Method: "IndexCache: Accelerating Sparse Attention via Cross-Layer Index
+ * Reuse" (gist.science es/pt/it/de editions of the paper summary).
+ *  - DSA layer (technical summary §1 on every edition): a lightning indexer
+ *    scores every previous token for each query, a per-row top-k keeps the k
+ *    most relevant positions, and core attention runs over those k only.
+ *  - IndexCache (technical summary §2, "Arquitectura del Método" on the es
+ *    edition, "Arquitetura" on pt): a binary pattern splits the layers into
+ *    Full (F) layers, which run indexer + top-k and store the index set, and
+ *    Shared (S) layers, which skip both and reuse the set of the nearest
+ *    preceding F layer - one conditional branch in the inference loop.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers except `pattern`, `layers`, `shape`, `stats` and the size
+ *    outputs are DEVICE pointers, 16-byte aligned, rows contiguous.  The
+ *    caller owns every buffer; the library never allocates, frees or
+ *    synchronises.  Work is enqueued on `stream` (0 = the null stream) and is
+ *    complete when the caller synchronises that stream.
+ *  - Query row t of sequence b sits at absolute position
+ *    pos(b,t) = ctx_len[b] - T + t and sees keys 0..pos (causal).  Callers
+ *    must keep T <= ctx_len[b] <= Lmax; the kernels clamp out-of-range values
+ *    instead of faulting, the results of such rows are unspecified.
+ *  - Arguments are validated on the host before anything is launched.  A
+ *    failing check returns a non-zero status, launches nothing and leaves a
+ *    message for dsa_last_error().  A failed launch returns DSA_ERR_HIP.
+ *  - Calls are re-entrant across host threads and streams as long as each
+ *    in-flight call has its own outputs and workspace.  The only global state
+ *    is the per-thread error message.
+ */
+#ifndef DSA_INDEXCACHE_H
+#define DSA_INDEXCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad pattern */
+  DSA_ERR_UNSUPPORTED = 2, /* a shape / dtype combination with no kernel     */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
+  DSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed      */
+} dsa_status_t;
+
+typedef enum dsa_dtype {
+  DSA_BF16 = 0,     /* bfloat16                                              */
+  DSA_FP8_E4M3 = 1  /* OCP fp8 e4m3 ("fn") codes with one fp32 scale per row */
+} dsa_dtype_t;
+
+/* Message describing the last non-OK status returned on this host thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* dsa_last_error(void);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* dsa_version(void);
+
+/*
+ * Lightning-indexer scores (technical summary §1: the indexer scores all
+ * previous tokens of every query; the form used is the DSA one)
+ *
+ *   scores[b,t,s] = sum_h w[b,t,h] * ReLU( q[b,t,h,:] . k[b,s,:] )  for s <= pos(b,t)
+ *   scores[b,t,s] = -inf                                            for pos(b,t) < s < Lmax
+ *
+ * q        [B,T,H,D] `dtype` elements.
+ * q_scale  [B,T,H] fp32 per-row dequantisation scale (> 0) if dtype is
+ *          DSA_FP8_E4M3 (real q = code * scale), must be NULL for DSA_BF16.
+ * w        [B,T,H] fp32 head weights, any sign (applied after the ReLU).
+ * k        [B,Lmax,D] `dtype` elements (the indexer key cache).
+ * k_scale  [B,Lmax] fp32 per-row scale (> 0) for fp8, NULL for bf16.
+ * ctx_len  [B] int32 (device).
+ * scores   [B,T,ld_scores] fp32 output; columns 0..Lmax-1 are written.
+ * Supported: D in {64,128}, 1 <= H <= 64, ld_scores >= Lmax and a multiple
+ * of 4.  Products are exact in fp32 and accumulate in fp32.
+ */
+dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t dtype, const float* q_scale,
+                                const float* w, const void* k, const float* k_scale,
+                                const int32_t* ctx_len, int B, int T, int H, int D, int Lmax,
+                                float* scores, int64_t ld_scores, hipStream_t stream);
+
+/*
+ * Per-row top-k (technical summary §1: keep the k most relevant tokens).
+ * For each row the k visible positions (0..pos(b,t)) with the highest score
+ * are written in ASCENDING position order; equal scores are broken toward
+ * the lower position; rows with fewer than k visible positions are padded
+ * with -1.  Scores are compared as fp32 values (-0 == +0); NaN is not
+ * allowed.
+ * scores [B,T,ld_scores] fp32 (only columns 0..pos(b,t) are read),
+ * idx    [B,T,k] int32 output.  1 <= k <= 16384, ld_scores multiple of 4.
+ * workspace: dsa_topk_workspace_size bytes (may be 0 / NULL when 0).
+ */
+dsa_status_t dsa_topk_workspace_size(int B, int T, int Lmax, int k, size_t* bytes);
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx_len, int B,
+                      int T, int Lmax, int k, int32_t* idx, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sparse MLA attention over the selected latent rows (technical summary §1:
+ * core attention restricted to the k selected tokens, O(Lk)).  Absorbed MLA:
+ * one latent row of d_qk values per token is shared by all Hq heads; logits
+ * use all d_qk columns, values the first d_v columns:
+ *
+ *   logit_j = scale * q[b,t,h,:] . kv[b, idx[b,t,j], :]   for valid j
+ *   out[b,t,h,:] = sum_j softmax(logit)_j * kv[b, idx[b,t,j], 0:d_v]
+ *   lse[b,t,h]   = log(sum_j exp(logit_j))                 (natural log)
+ *
+ * An entry j is valid when 0 <= idx[b,t,j] <= pos(b,t); others (the -1
+ * padding) are skipped.  A row with no valid entry gives out = 0, lse = -inf.
+ * q [B,T,Hq,d_qk] bf16, kv [B,Lmax,d_qk] bf16, idx [B,T,k] int32,
+ * out [B,T,Hq,d_v] bf16 (round to nearest even from fp32),
+ * lse [B,T,Hq] fp32 or NULL.  Softmax and accumulation are fp32.
+ * Supported: d_qk == 576, d_v == 512, Hq a multiple of 16, 1 <= k <= 65536.
+ */
+dsa_status_t dsa_sparse_attn_workspace_size(int B, int T, int Hq, int k, int d_v,
+                                            size_t* bytes);
+dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
+                             const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k,
+                             int d_qk, int d_v, float scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One layer's device tensors for indexcache_run_stack.  q_idx / w / k_idx
+ * (and the fp8 scales) are read on F layers only; q / kv / out (and lse)
+ * only when shape->Hq > 0. */
+typedef struct dsa_layer {
+  const void* q_idx;         /* [B,T,H,D]        */
+  const float* q_idx_scale;  /* [B,T,H] or NULL  */
+  const float* w;            /* [B,T,H]          */
+  const void* k_idx;         /* [B,Lmax,D]       */
+  const float* k_idx_scale;  /* [B,Lmax] or NULL */
+  const void* q;             /* [B,T,Hq,d_qk]    */
+  const void* kv;            /* [B,Lmax,d_qk]    */
+  void* out;                 /* [B,T,Hq,d_v]     */
+  float* lse;                /* [B,T,Hq] or NULL */
+} dsa_layer_t;
+
+typedef struct dsa_stack_shape {
+  int B, T, H, D, Lmax, k;
+  int Hq, d_qk, d_v;       /* Hq == 0: indexer + top-k only, no attention */
+  dsa_dtype_t idx_dtype;
+  float scale;             /* softmax scale of the sparse attention       */
+} dsa_stack_shape_t;
+
+typedef struct dsa_stack_stats {
+  int n_indexer_calls;     /* == number of 'F' in the pattern */
+  int n_topk_calls;
+  int n_attn_calls;
+} dsa_stack_stats_t;
+
+/*
+ * The IndexCache layer loop (technical summary §2).  pattern is a host
+ * string of n_layers characters, each 'F' or 'S', starting with 'F' (an S
+ * layer inherits from the nearest PRECEDING F layer, so a leading S has
+ * nothing to inherit and is rejected).  For layer l:
+ *   'F': scores = dsa_indexer_scores(layer l) into score_buf, then
+ *        dsa_topk into idx_buf              (the index cache is written)
+ *   'S': nothing                            (idx_buf is reused in place)
+ *   then, if Hq > 0, dsa_sparse_attn(layer l, idx_buf).
+ * idx_buf [B,T,k] int32 holds the last F layer's set when the call returns.
+ * score_buf [B,T,ld_scores] fp32 scratch, workspace sized by
+ * indexcache_stack_workspace_size.  stats (host, may be NULL) receives the
+ * number of kernels of each kind that were enqueued.
+ */
+dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* shape, size_t* bytes);
+dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_layer_t* layers,
+                                  const dsa_stack_shape_t* shape, const int32_t* ctx_len,
+                                  int32_t* idx_buf, float* score_buf, int64_t ld_scores,
+                                  void* workspace, size_t workspace_bytes,
+                                  dsa_stack_stats_t* stats, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_INDEXCACHE_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any GPU work (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dsa_sparse_attention_lightning_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if not f.endswith(".h"):
+            continue
+        src = open(os.path.join(inc, f)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M):
+            if m.group(1) not in ("if", "while", "for", "sizeof"):
+                names.append(m.group(1))
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "indexcache_run_stack",
+                 "dsa_last_error", "dsa_topk_workspace_size", "dsa_sparse_attn_workspace_size",
+                 "indexcache_stack_workspace_size", "dsa_version"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.dsa_version()
+
+
+def _err(lib):
+    return lib.dsa_last_error().decode()
+
+
+def test_topk_rejects_bad_k(lib):
+    st = lib.dsa_topk(16, 4096, 16, 1, 1, 4096, 0, 16, None, 0, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and "k must be" in _err(lib)
+    st = lib.dsa_topk(16, 4096, 16, 1, 1, 4096, 20000, 16, None, 0, None)
+    assert st == _lib.DSA_ERR_UNSUPPORTED
+
+
+def test_topk_rejects_null_and_misaligned(lib):
+    assert lib.dsa_topk(None, 4096, 16, 1, 1, 4096, 8, 16, None, 0, None) == 1
+    assert "scores is NULL" in _err(lib)
+    assert lib.dsa_topk(18, 4096, 16, 1, 1, 4096, 8, 16, None, 0, None) == 1
+    assert "aligned" in _err(lib)
+    assert lib.dsa_topk(16, 4094, 16, 1, 1, 4094, 8, 16, None, 0, None) == 1  # ld % 4
+
+
+def test_indexer_rejects_unsupported(lib):
+    f = lib.dsa_indexer_scores
+    assert f(16, 0, None, 16, 16, None, 16, 1, 1, 64, 96, 128, 16, 128, None) == 2   # D = 96
+    assert f(16, 0, None, 16, 16, None, 16, 1, 1, 65, 128, 128, 16, 128, None) == 2  # H = 65
+    assert f(16, 1, None, 16, 16, None, 16, 1, 1, 64, 128, 128, 16, 128, None) == 1  # fp8 no scale
+    assert "scale" in _err(lib)
+    assert f(16, 0, 16, 16, 16, None, 16, 1, 1, 64, 128, 128, 16, 128, None) == 1   # bf16 + scale
+    assert f(16, 7, None, 16, 16, None, 16, 1, 1, 64, 128, 128, 16, 128, None) == 1  # dtype
+    assert f(16, 0, None, 16, 16, None, 16, 1, 200, 64, 128, 128, 16, 128, None) == 1  # T > Lmax
+
+
+def test_attn_rejects_unsupported(lib):
+    f = lib.dsa_sparse_attn
+    assert f(16, 16, 16, 16, 1, 1, 128, 100, 8, 512, 512, 0.1, 16, None, None, 0, None) == 2
+    assert f(16, 16, 16, 16, 1, 1, 100, 100, 8, 576, 512, 0.1, 16, None, None, 0, None) == 2
+    assert f(16, 16, 16, 16, 1, 1, 128, 100, 8, 576, 512, -1.0, 16, None, None, 0, None) == 1
+    need = ctypes.c_size_t()
+    assert lib.dsa_sparse_attn_workspace_size(8, 1, 128, 2048, 512, ctypes.byref(need)) == 0
+    if need.value:
+        assert f(16, 16, 16, 16, 8, 1, 128, 4096, 2048, 576, 512, 0.1, 16, None, None, 0,
+                 None) == _lib.DSA_ERR_WORKSPACE
+
+
+def _stack_args(pattern, n):
+    layers = (_lib.Layer * n)()
+    for i in range(n):
+        layers[i] = _lib.Layer(16, None, 16, 16, None, 16, 16, 16, None)
+    shape = _lib.StackShape(1, 1, 64, 128, 4096, 2048, 128, 576, 512, 0, 0.1)
+    return pattern.encode(), n, layers, shape
+
+
+@pytest.mark.parametrize("pattern,n,msg", [("SFFF", 4, "start with 'F'"), ("FSX", 3, "neither"),
+                                           ("FSS", 4, "length"), ("FSSSS", 4, "length")])
+def test_stack_rejects_bad_patterns(lib, pattern, n, msg):
+    p, n, layers, shape = _stack_args(pattern, n)
+    st = lib.indexcache_run_stack(p, n, layers, ctypes.byref(shape), 16, 16, 16, 4096, 16,
+                                  1 << 30, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG
+    assert msg in _err(lib)
+
+
+def test_stack_rejects_small_workspace(lib):
+    p, n, layers, shape = _stack_args("FSSS", 4)
+    need = ctypes.c_size_t()
+    assert lib.indexcache_stack_workspace_size(ctypes.byref(shape), ctypes.byref(need)) == 0
+    if need.value == 0:
+        pytest.skip("no workspace needed at this shape")
+    st = lib.indexcache_run_stack(p, n, layers, ctypes.byref(shape), 16, 16, 16, 4096, 16,
+                                  need.value - 1, None, None)
+    assert st == _lib.DSA_ERR_WORKSPACE

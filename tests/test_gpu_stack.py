@@ -1,0 +1,118 @@
+"""The IndexCache layer stack on the GPU against the fp64 oracle (tiny decode workload)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dsa_sparse_attention_lightning_amd as dsa
+from dsa_sparse_attention_lightning_amd import inputs as gen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def build_layers(s: gen.Shape):
+    qi = gen.make_indexer_query(s, DEV)
+    kb = gen.make_key_base(s, DEV)
+    layers = []
+    for l in range(s.n_layers):
+        ki = gen.make_indexer_keys(s, l, kb, DEV)
+        q, kv = gen.make_mla_layer(s, l, DEV)
+        layers.append(dict(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w, k_idx=ki.k,
+                           k_idx_scale=ki.k_scale, q=q, kv=kv,
+                           out=torch.empty((s.B, s.T, s.Hq, s.d_v), dtype=torch.bfloat16,
+                                           device=DEV),
+                           lse=torch.empty((s.B, s.T, s.Hq), dtype=torch.float32, device=DEV)))
+    return layers
+
+
+def shape_kwargs(s):
+    return dict(B=s.B, T=s.T, H=s.H, D=s.D, Lmax=s.Lmax, k=s.k, Hq=s.Hq,
+                idx_dtype=s.idx_dtype, scale=s.scale)
+
+
+def oracle_layers(layers, s):
+    out = []
+    for L in layers:
+        out.append(dict(q_idx=parity.host_real(L["q_idx"], L["q_idx_scale"]),
+                        w=L["w"].cpu().double().numpy(),
+                        k_idx=parity.host_real(L["k_idx"], L["k_idx_scale"]),
+                        q=parity.host_real(L["q"]), kv=parity.host_real(L["kv"])))
+    return out
+
+
+@pytest.mark.parametrize("pattern", ["FSSS", "FFFF", "FSFS"])
+def test_tiny_stack_against_oracle(pattern):
+    s = gen.CONFIGS[0]
+    say("stack C0 pattern", pattern)
+    layers = build_layers(s)
+    ctx_t = gen.ctx_lens(s, DEV)
+    ctx = [s.ctx] * s.B
+    st = dsa.Stack(pattern, layers, ctx_t, **shape_kwargs(s))
+    stats = st.run()
+    torch.cuda.synchronize()
+    assert stats["n_indexer_calls"] == pattern.count("F")
+    assert stats["n_topk_calls"] == pattern.count("F")
+    assert stats["n_attn_calls"] == len(pattern)
+    # GPU index set of every F layer through the standalone entry points
+    gpu_idx = {}
+    for l, c in enumerate(pattern):
+        if c == "F":
+            L = layers[l]
+            sc = dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx_t, L["q_idx_scale"],
+                                    L["k_idx_scale"])
+            gpu_idx[l] = dsa.topk(sc, ctx_t, s.k).cpu().numpy()
+    last_f = max(gpu_idx)
+    assert np.array_equal(st.idx_buf.cpu().numpy(), gpu_idx[last_f])
+    ol = oracle_layers(layers, s)
+    ref = oracle.run_stack(pattern, ol, ctx, s.k, s.scale, s.d_v)
+    assert ref["n_indexer_calls"] == stats["n_indexer_calls"]
+    used = None
+    for l, c in enumerate(pattern):
+        if c == "F":
+            used = gpu_idx[l]
+            sc = oracle.indexer_scores(ol[l]["q_idx"], ol[l]["w"], ol[l]["k_idx"], ctx)
+            parity.check_topk_boundary(used, sc, ctx, s.k)
+        # attention of layer l on the index set the GPU used
+        ro, rl = oracle.sparse_attn(ol[l]["q"], ol[l]["kv"], used, ctx, s.scale, s.d_v)
+        parity.check_attn(layers[l]["out"].float().cpu().numpy(), layers[l]["lse"].cpu().numpy(),
+                          ro, rl)
+        # and end to end against the oracle's own stack
+        parity.check_attn(layers[l]["out"].float().cpu().numpy(), None, ref["out"][l], None)
+
+
+def test_shared_layers_match_all_f_on_identical_keys():
+    """With the same keys in every layer, every pattern reproduces all-F outputs bit for bit."""
+    s = gen.CONFIGS[0]
+    layers = build_layers(s)
+    for L in layers[1:]:
+        L["k_idx"] = layers[0]["k_idx"]
+    ctx_t = gen.ctx_lens(s, DEV)
+    outs = {}
+    for p in ("FFFF", "FSSS", "FSFS"):
+        dsa.Stack(p, layers, ctx_t, **shape_kwargs(s)).run()
+        torch.cuda.synchronize()
+        outs[p] = [L["out"].clone() for L in layers]
+    for p in ("FSSS", "FSFS"):
+        for a, b in zip(outs[p], outs["FFFF"]):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bad", ["SFFF", "FSX", "FSS", "FSSSS"])
+def test_bad_pattern_rejected_before_launch(bad):
+    s = gen.CONFIGS[0]
+    layers = build_layers(s)
+    st = dsa.Stack("FSSS", layers, gen.ctx_lens(s, DEV), **shape_kwargs(s))
+    st.pattern = bad.encode()
+    st.n_layers = 4
+    with pytest.raises(dsa.DSAError) as e:
+        st.run()
+    assert e.value.status == 1
