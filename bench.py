@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Decode throughput of the IndexCache / DSA hot path on one MI355X.
+
+Workload (default): long-context decode, a 48-layer stack with F layers at
+0,3,7,11,15,19,23,27,31,35,40,44 (S elsewhere), batch 8, context 131072,
+indexer 64 heads x 128 fp8 with per-row scales, top-2048, sparse MLA with 128
+heads over 576-wide bf16 latent rows.  One step = one decode token for every
+sequence through all 48 layers: indexer + top-k on F layers, sparse attention
+on every layer.  Inputs are seeded synthetic tensors resident in HBM before
+the timed region.
+
+Also reported on the same line:
+  * the same stack with all-F and with 'FSSS' x 12;
+  * indexer + top-k time per layer and per 4-layer group (Hq = 0 stacks);
+  * per-kernel average durations from HIP events on the launch stream, and the
+    roofline of the dominant kernel;
+  * the prefill chunk (8192 queries on a 65536-token context, fp8, plus the
+    same shape in bf16): indexer scores TFLOP/s and top-k time;
+  * the fp64 CPU oracle timed on a bounded sample on this host.
+
+python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + indexer+top-k µs/layer at 128K ctx, FSSS vs all-F"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def event_time_ms(fn, reps: int, warm: int = 2) -> float:
+    """Average milliseconds per call of fn() over `reps` back-to-back calls,
+    bracketed by HIP events on torch's current stream (the launch stream)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def build_decode_workload(s, dev):
+    import torch
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    t0 = time.time()
+    qi = gen.make_indexer_query(s, dev)
+    kb = gen.make_key_base(s, dev)
+    layers = []
+    for l in range(s.n_layers):
+        ki = gen.make_indexer_keys(s, l, kb, dev)
+        q, kv = gen.make_mla_layer(s, l, dev)
+        layers.append(dict(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w, k_idx=ki.k,
+                           k_idx_scale=ki.k_scale, q=q, kv=kv,
+                           out=torch.empty((s.B, s.T, s.Hq, s.d_v), dtype=torch.bfloat16,
+                                           device=dev),
+                           lse=torch.empty((s.B, s.T, s.Hq), dtype=torch.float32, device=dev)))
+    del kb
+    torch.cuda.synchronize()
+    log(f"workload built in {time.time() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB on device)")
+    return layers
+
+
+def shape_kw(s, attn=True):
+    return dict(B=s.B, T=s.T, H=s.H, D=s.D, Lmax=s.Lmax, k=s.k, Hq=s.Hq if attn else 0,
+                idx_dtype=s.idx_dtype, scale=s.scale)
+
+
+def time_stack(stack, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        stack.run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        stats = stack.run()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps, stats
+
+
+def indexer_bytes(s):
+    e = 1 if s.idx_dtype == "fp8" else 2
+    per_key = s.D * e + (4 if s.idx_dtype == "fp8" else 0) + 4        # key row (+scale) + score
+    per_seq = s.Lmax * per_key + s.H * s.D * e + s.H * 4 * (2 if s.idx_dtype == "fp8" else 1)
+    return s.B * s.T * per_seq if s.T == 1 else None
+
+
+def attn_bytes_flops(s):
+    per_row = (s.k * s.d_qk * 2 + s.k * 4 + s.Hq * s.d_qk * 2 + s.Hq * s.d_v * 2 + s.Hq * 4)
+    flops = 2.0 * s.Hq * s.k * (s.d_qk + s.d_v)
+    return s.B * s.T * per_row, s.B * s.T * flops
+
+
+def decode_bench(args, dev):
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+
+    s = gen.CONFIGS[args.config]
+    layers = build_decode_workload(s, dev)
+    ctx = gen.ctx_lens(s, dev)
+    pats = {"config": s.pattern, "all-F": "F" * s.n_layers,
+            "FSSS": gen.tile_pattern("FSSS", s.n_layers)}
+    res = {}
+    for name, p in pats.items():
+        st = dsa.Stack(p, layers, ctx, **shape_kw(s))
+        ms, stats = time_stack(st, args.steps, args.warmup)
+        st_i = dsa.Stack(p, layers, ctx, **shape_kw(s, attn=False))
+        ms_i, _ = time_stack(st_i, args.steps, args.warmup)
+        res[name] = dict(pattern=p, ms_per_step=ms, tokens_per_s=s.B / (ms * 1e-3),
+                         n_indexer_calls=stats["n_indexer_calls"],
+                         indexer_topk_ms_per_step=ms_i,
+                         indexer_topk_us_per_layer=ms_i * 1e3 / s.n_layers,
+                         indexer_topk_us_per_group4=ms_i * 1e3 / (s.n_layers / 4))
+        log(f"{name:7s} {ms:8.3f} ms/step  {s.B / (ms * 1e-3):9.0f} tok/s  "
+            f"indexer+topk {ms_i * 1e3 / s.n_layers:7.2f} us/layer  F={stats['n_indexer_calls']}")
+    cut = 1.0 - res["FSSS"]["indexer_topk_ms_per_step"] / res["all-F"]["indexer_topk_ms_per_step"]
+
+    # ---- per-kernel durations (events around back-to-back launches)
+    f_layers = [l for l, c in enumerate(s.pattern) if c == "F"]
+    score = torch.empty((s.B, s.T, dsa.ld_for(s.Lmax)), dtype=torch.float32, device=dev)
+    idx = torch.empty((s.B, s.T, s.k), dtype=torch.int32, device=dev)
+    reps = max(24, 2 * len(f_layers))
+
+    def run_idx(i=0):
+        L = layers[f_layers[i % len(f_layers)]]
+        dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx, L["q_idx_scale"],
+                           L["k_idx_scale"], out=score)
+
+    t_idx = event_time_ms(run_idx, reps)
+    t_topk = event_time_ms(lambda i=0: dsa.topk(score[..., :s.Lmax], ctx, s.k, out=idx), reps)
+
+    def run_attn(i=0):
+        L = layers[i % s.n_layers]
+        dsa.sparse_attn(L["q"], L["kv"], idx, ctx, s.scale, out=L["out"], lse=L["lse"])
+
+    t_attn = event_time_ms(run_attn, max(48, reps))
+    ib = indexer_bytes(s)
+    ab, af = attn_bytes_flops(s)
+    nF = s.pattern.count("F")
+    kernels = {
+        "indexer_decode": dict(us=t_idx * 1e3, launches_per_step=nF, bytes=ib,
+                               gbs=ib / (t_idx * 1e-3) / 1e9),
+        "topk": dict(us=t_topk * 1e3, launches_per_step=nF,
+                     bytes=s.B * s.Lmax * 4 + s.B * s.k * 4,
+                     gbs=(s.B * s.Lmax * 4 + s.B * s.k * 4) / (t_topk * 1e-3) / 1e9),
+        "sparse_mla": dict(us=t_attn * 1e3, launches_per_step=s.n_layers, bytes=ab, flops=af,
+                           gbs=ab / (t_attn * 1e-3) / 1e9,
+                           tflops=af / (t_attn * 1e-3) / 1e12),
+    }
+    for k_, v in kernels.items():
+        v["us_per_step"] = v["us"] * v["launches_per_step"]
+        log(f"kernel {k_:15s} {v['us']:8.2f} us x {v['launches_per_step']:2d}  "
+            f"{v['gbs']:8.1f} GB/s")
+    dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
+    kd = kernels[dom]
+    roof = dict(kernel=dom, bound="hbm", achieved=round(kd["gbs"], 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(kd["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
+                per_launch_bytes=kd["bytes"], avg_launch_us=round(kd["us"], 3))
+    return s, layers, res, cut, kernels, roof
+
+
+def prefill_bench(dev, reps=5):
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    out = {}
+    base = gen.CONFIGS[2]
+    for dt in ("fp8", "bf16"):
+        s = gen.Shape(2, base.name, 1, "F", B=base.B, T=base.T, ctx=base.ctx, H=base.H,
+                      D=base.D, idx_dtype=dt, k=base.k)
+        qi = gen.make_indexer_query(s, dev)
+        ki = gen.make_indexer_keys(s, 0, gen.make_key_base(s, dev), dev)
+        ctx = gen.ctx_lens(s, dev)
+        score = torch.empty((s.B, s.T, dsa.ld_for(s.Lmax)), dtype=torch.float32, device=dev)
+        idx = torch.empty((s.B, s.T, s.k), dtype=torch.int32, device=dev)
+        t_i = event_time_ms(lambda i=0: dsa.indexer_scores(qi.q, qi.w, ki.k, ctx, qi.q_scale,
+                                                           ki.k_scale, out=score), reps, 1)
+        t_k = event_time_ms(lambda i=0: dsa.topk(score[..., :s.Lmax], ctx, s.k, out=idx), reps, 1)
+        pos0 = s.ctx - s.T
+        pairs = sum(pos0 + t + 1 for t in range(s.T))
+        flops = 2.0 * s.H * s.D * pairs * s.B
+        tf = flops / (t_i * 1e-3) / 1e12
+        out[dt] = dict(indexer_ms=round(t_i, 4), topk_ms=round(t_k, 4),
+                       algorithmic_tflop=round(flops / 1e12, 4), tflops=round(tf, 1),
+                       frac_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4),
+                       frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
+        log(f"prefill {dt}: indexer {t_i:.3f} ms ({tf:.0f} TFLOP/s, "
+            f"{tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak), top-k {t_k:.3f} ms")
+        del qi, ki, score, idx
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(s, layers, budget_s):
+    """The fp64 oracle, as it stands, on sequence 0 of the same workload."""
+    import numpy as np
+    import oracle
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    b = 0
+    t_f, t_s = [], []
+    idx = None
+    q_idx = oracle.dequant_fp8_rows(gen.bits(layers[0]["q_idx"][b:b + 1]),
+                                    layers[0]["q_idx_scale"][b:b + 1].cpu().numpy())
+    w = layers[0]["w"][b:b + 1].cpu().double().numpy()
+    ctx = [s.ctx]
+    start = time.time()
+    for l, c in enumerate(s.pattern):
+        if time.time() - start > budget_s and t_f and t_s:
+            break
+        L = layers[l]
+        q = oracle.bf16_bits_to_f64(gen.bits(L["q"][b:b + 1]))
+        kv = oracle.bf16_bits_to_f64(gen.bits(L["kv"][b:b + 1]))
+        kk = None
+        if c == "F":
+            kk = oracle.dequant_fp8_rows(gen.bits(L["k_idx"][b:b + 1]),
+                                         L["k_idx_scale"][b:b + 1].cpu().numpy())
+        t0 = time.perf_counter()
+        if c == "F":
+            sc = oracle.indexer_scores(q_idx, w, kk, ctx)
+            idx = oracle.topk(sc, ctx, s.k)
+        oracle.sparse_attn(q, kv, idx, ctx, s.scale, s.d_v)
+        dt = time.perf_counter() - t0
+        (t_f if c == "F" else t_s).append(dt)
+        del q, kv, kk
+    nF = s.pattern.count("F")
+    per_token = nF * float(np.mean(t_f)) + (s.n_layers - nF) * float(np.mean(t_s))
+    return dict(value=round(1.0 / per_token, 4), unit="tokens/s", cores=int(threads),
+                kind="oracle",
+                sample=(f"sequence 0 of {s.B}, layers 0..{len(t_f) + len(t_s) - 1} of the "
+                        f"{s.n_layers}-layer stack ({len(t_f)} F, {len(t_s)} S timed), projected "
+                        f"to {nF} F + {s.n_layers - nF} S layers for one token; fp64 numpy, "
+                        f"{os.cpu_count()} host cores"),
+                seconds_per_F_layer=round(float(np.mean(t_f)), 4),
+                seconds_per_S_layer=round(float(np.mean(t_s)), 4))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share of the path: --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported; run with --gpus 1", flush=True)
+        sys.exit(2)
+
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", flush=True)
+        sys.exit(1)
+    dsa.library()  # fail loudly if the HIP library is missing
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    s, layers, res, cut, kernels, roof = decode_bench(args, dev)
+    main_res = res["config"]
+    prefill = None if args.no_prefill else prefill_bench(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(s, layers, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 indexer, bf16 attention, fp32 accumulate",
+        "data": "synthetic: seeded N(0,1) queries/keys/latents, U(0,1) head weights, "
+                "indexer keys correlated 0.9 across layers",
+        "config": {"workload": f"{s.name}: {s.n_layers} layers, batch {s.B}, context {s.ctx}, "
+                               f"indexer {s.H}x{s.D} {s.idx_dtype}, top-{s.k}, "
+                               f"MLA {s.Hq} heads x {s.d_qk} bf16",
+                   "pattern": s.pattern, "batch": s.B, "context": s.ctx},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "patterns": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                         for kk, vv in v.items()} for k, v in res.items()},
+        "fsss_vs_allf_indexer_topk_cut": round(cut, 4),
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in kernels.items()},
+        "prefill": prefill,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
