@@ -25,6 +25,13 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 
+# Per-source extra flags.  sparse_mla keeps its MFMA accumulators in ordinary
+# VGPRs: its online-softmax rescale touches the O accumulator with VALU
+# instructions, and AGPR-resident accumulators would be copied out and back
+# around that code on every tile.
+EXTRA = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -39,7 +46,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -9,17 +9,24 @@
 // online-softmax accumulator.
 //
 // Work split: a workgroup owns one query row, WAVES*16 heads and one slice of
-// the k selected rows (split-KV; a combine kernel merges the slices by their
+// the k selected rows (split-KV; a combine kernel merges slices by their
 // log-sum-exp).  Each wave owns 16 heads: its query block stays in registers
-// (72 VGPRs) and its O^T accumulator [512 x 16] is 128 fp32 per lane.  Rows
-// are processed 32 at a time; the workgroup gathers the 32 rows into LDS in
-// two layouts:
-//   Ks [32][576]  row-major        -> operand A of S^T = Ks . q^T
-//   Vt [512][32]  dim-major        -> operand A of O^T += Vt . P^T
-// Vt is produced with an in-register 8x8 transpose of the gathered 16-byte
-// pieces.  The 32 rows are stored in Vt in the order kappa that matches where
-// the S^T accumulator leaves them (lane group g holds rows 4g..4g+3 and
-// 16+4g..16+4g+3), so P^T feeds the second product without any shuffle.
+// (operand B of S^T = K . q^T) and its O^T accumulator [512 x 16] is 128 fp32
+// per lane.  Rows are processed 32 at a time:
+//   * the 32 selected rows are gathered straight from HBM into LDS with
+//     16-byte LDS-DMA loads (global_load_lds_dwordx4), double-buffered so the
+//     next tile streams in while the current one is multiplied;
+//   * the tile is stored row-major with a row pitch of 73 16-byte chunks
+//     (1168 B): the 16-byte row reads of S^T hit 8 distinct bank groups per
+//     8 lanes, the transposing reads at most 2-way conflicts, and every LDS
+//     address is a per-lane base plus an immediate;
+//   * S^T reads 16-byte row fragments (operand A);
+//   * O^T += V^T . P^T takes operand A (8 consecutive rows of one latent dim
+//     per lane) with two transposing LDS reads (ds_read_b64_tr_b16) from the
+//     same row-major tile, and operand B straight from the S^T accumulator:
+//     the reduction order kappa = 8g + j is mapped to tile rows
+//     rho(kappa) = 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4), which is where
+//     the 16x16 accumulator of S^T leaves them.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -29,31 +36,58 @@ namespace {
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRows = 32;                 // rows per tile
-constexpr int kKsPitch = kDqk + 8;        // bf16 elements (1168 B: spreads LDS banks)
-constexpr int kVtPitch = kRows + 8;       // bf16 elements (80 B)
-constexpr int kChunks = kDqk / 8;         // 16-byte pieces per row (72)
-constexpr int kVChunks = kDv / 8;         // 64
+constexpr int kRowBytes = kDqk * 2;       // 1152
+constexpr int kChunks = kDqk / 8;         // 16-byte chunks per row (72)
+constexpr int kPitchChunks = kChunks + 1; // LDS row pitch in 16-byte chunks (73)
+constexpr int kPitch = kPitchChunks * 16; // 1168
+constexpr int kTileSlots = kRows * kPitchChunks;                  // 2336
+constexpr int kTileLoads = (kTileSlots + kWave - 1) / kWave;      // 37 wave-loads
+constexpr int kTileBytes = kTileLoads * kWave * 16;               // 37888 (with slack)
+constexpr int kMaxSplitRows = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;   // log2 headroom of the lazy softmax rescale
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
 
 template <int WAVES>
 struct AttnSmem {
-  __bf16 ks[kRows * kKsPitch];
-  __bf16 vt[kDv * kVtPitch];
-  int32_t rowidx[kRows];
+  __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
+  __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
+  int32_t rows[kMaxSplitRows];
 };
 
-// Row r of a tile sits at position kappa(r) in Vt.
-__device__ __forceinline__ int tile_row_of(int q, int j) {  // kappa = 8q + j -> row
-  return (j < 4) ? (4 * q + j) : (16 + 4 * q + (j - 4));
+// Issue the LDS-DMA gather of one 32-row tile: the 16-byte LDS slots of the
+// tile are written in order, 64 per wave instruction; slot p holds chunk
+// p % 73 of row p / 73.  The pad slot of each row and the slack after the
+// last row receive a harmless copy of chunk 0 of the row.
+template <int WAVES>
+__device__ __forceinline__ void gather_tile(unsigned char* tile, const __bf16* kvb,
+                                            const int32_t* rows, int lane, int wave) {
+  for (int i = wave; i < kTileLoads; i += WAVES) {
+    const int p = i * kWave + lane;
+    int r = p / kPitchChunks;
+    int c = p - r * kPitchChunks;
+    if (c >= kChunks) c = 0;
+    if (r >= kRows) { r = 0; c = 0; }
+    const int src = max(rows[r], 0);
+    __builtin_amdgcn_global_load_lds((const void*)(kvb + (int64_t)src * kDqk + 8 * c),
+                                     (lds_void*)(tile + i * kWave * 16), 16, 0, 0);
+  }
 }
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ ctx_len, int T, int Hq, int Lmax, int k, int rows_per_split,
     float scale_log2, __bf16* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse, int n_split) {
+    float* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups) {
   constexpr int NT = WAVES * kWave;
   __shared__ AttnSmem<WAVES> sm;
   const int tid = threadIdx.x;
@@ -61,17 +95,30 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
   const int wave = tid / kWave;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int row = blockIdx.x;  // b * T + t
+  // blockIdx.x -> (row, head group, split); the splits of one (row, head
+  // group) are spread so consecutive workgroups land on different XCDs.
+  const int bid = blockIdx.x;
+  const int split = bid % n_split;
+  const int rg = bid / n_split;
+  const int hgi = rg % head_groups;
+  const int row = rg / head_groups;  // b * T + t
   const int b = row / T;
   const int t = row - b * T;
-  const int head = blockIdx.y * (WAVES * 16) + wave * 16 + c16;
-  const int split = blockIdx.z;
+  const int head = hgi * (WAVES * 16) + wave * 16 + c16;
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   const int j0 = split * rows_per_split;
-  const int j1 = min(k, j0 + rows_per_split);
+  const int nrows = max(0, min(k, j0 + rows_per_split) - j0);
+  const int ntiles = (nrows + kRows - 1) / kRows;
 
-  // Query fragments: operand B of S^T (column = head, reduction = dims).
-  // Lane group g covers dims [144 g, 144 g + 144).
+  // Selected rows of this slice, validated once (invalid / padding -> -1).
+  const int32_t* ib = idx + (int64_t)row * k + j0;
+  for (int j = tid; j < ntiles * kRows; j += NT) {
+    int v = (j < nrows) ? ib[j] : -1;
+    if (v < 0 || (int64_t)v > pos || v >= Lmax) v = -1;
+    sm.rows[j] = v;
+  }
+  // Query fragments: operand B of S^T (column = head, reduction = dims);
+  // lane group g covers dims [144 g, 144 g + 144).
   bf16x8 qf[18];
   {
     const __bf16* qp = q + ((int64_t)row * Hq + head) * kDqk + 144 * g;
@@ -82,54 +129,35 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
 #pragma unroll
   for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-
   const __bf16* kvb = kv + (int64_t)b * Lmax * kDqk;
-  const int32_t* ib = idx + (int64_t)row * k;
+  __syncthreads();
 
-  for (int r0 = j0; r0 < j1; r0 += kRows) {
-    // ---- gather 32 rows into LDS
-    if (tid < kRows) {
-      const int j = r0 + tid;
-      int v = (j < j1) ? ib[j] : -1;
-      if (v < 0 || (int64_t)v > pos || v >= Lmax) v = -1;
-      sm.rowidx[tid] = v;
-    }
-    __syncthreads();
-    for (int task = tid; task < 4 * kChunks; task += NT) {
-      const int qg = task / kChunks;   // kappa group: rows 4qg..4qg+3, 16+4qg..16+4qg+3
-      const int c = task - qg * kChunks;
-      i32x4 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = tile_row_of(qg, j);
-        const int src = max(sm.rowidx[r], 0);
-        v[j] = ld16(kvb + (int64_t)src * kDqk + 8 * c);
-        *reinterpret_cast<i32x4*>(&sm.ks[r * kKsPitch + 8 * c]) = v[j];
-      }
-      if (c < kVChunks) {
-        // 8 rows x 8 dims -> 8 dims x 8 rows (kappa order) by byte permutes
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-          i32x4 tv;
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            tv[p] = (int)__builtin_amdgcn_perm((uint32_t)v[2 * p + 1][d >> 1],
-                                               (uint32_t)v[2 * p][d >> 1], sel);
-          *reinterpret_cast<i32x4*>(&sm.vt[(8 * c + d) * kVtPitch + 8 * qg]) = tv;
-        }
-      }
-    }
-    __syncthreads();
+  // The first two tiles are requested together: a slice of 64 rows (the
+  // common decode case) then waits on a single round trip to HBM.
+  if (ntiles > 0) gather_tile<WAVES>(sm.tile0, kvb, sm.rows, lane, wave);
+  if (ntiles > 1) gather_tile<WAVES>(sm.tile1, kvb, sm.rows + kRows, lane, wave);
+  wait_vm_all();
+  __syncthreads();
 
-    // ---- S^T tile [32 rows x 16 heads] = Ks . q^T
+  // Per-lane LDS byte offsets that do not depend on the tile.
+  // S^T operand A: row (16 mb + c16), dims 144 g + 8 i.
+  // O^T operand A (transposing reads): source row 4g + (c16 >> 2) (+16),
+  // dims 16 mb + 4 (c16 & 3).
+  const int qk_base = c16 * kPitch + 288 * g;
+  const int tr_base = (4 * g + (c16 >> 2)) * kPitch + 8 * (c16 & 3);
+
+  auto compute = [&](const unsigned char* tile, int tbase) {
+    // ---- S^T [32 rows x 16 heads]
     f32x4 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const __bf16* ap = &sm.ks[(16 * mb + c16) * kKsPitch + 144 * g];
+      const unsigned char* ap = tile + qk_base + 16 * mb * kPitch;
 #pragma unroll
-      for (int i = 0; i < 18; ++i) acc = mfma16_bf16(as_bf16x8(ld16(ap + 8 * i)), qf[i], acc);
+      for (int i = 0; i < 18; ++i) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * i));
+        acc = mfma16_bf16(a, qf[i], acc);
+      }
       s[mb] = acc;
     }
     // ---- online softmax (log2 domain); lane holds rows 4g+r and 16+4g+r
@@ -138,50 +166,71 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = sm.rowidx[16 * mb + 4 * g + r] >= 0;
+        const bool valid = sm.rows[tbase + 16 * mb + 4 * g + r] >= 0;
         s[mb][r] = valid ? s[mb][r] * scale_log2 : -INFINITY;
         mt = fmaxf(mt, s[mb][r]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
     mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);
-    float alpha = 1.f;
-    float p[2][4];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[mb][r] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-      float ls = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[mb][r] = exp2f(s[mb][r] - m_new);
-          ls += p[mb][r];
-        }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-    }
-    if (alpha != 1.f) {
+    // Lazy rescaling: the reference max m_run only moves when a tile's max
+    // exceeds it by more than 2^kLazy.  P = 2^(s - m_run) then stays below
+    // 2^kLazy, and O, l and the log-sum-exp all use the same reference, so the
+    // result is the exact softmax; the O rescale (128 accumulators) runs only
+    // when some head's reference moves, which is rare after the first tile.
+    const bool need = mt > m_run + kLazy;
+    if (__any(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? exp2f(m_run - m_new) : 1.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) o[i] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
     }
-    // P^T operand: kappa = 8g + j  <->  rows 4g+j (j<4), 16+4g+j-4 (j>=4)
+    float p[2][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[mb][r] = (m_run == -INFINITY) ? 0.f : exp2f(s[mb][r] - m_run);
+        ls += p[mb][r];
+      }
+    l_run += ls;
     i32x4 pb;
     pb[0] = (int)pack_bf16x2(p[0][0], p[0][1]);
     pb[1] = (int)pack_bf16x2(p[0][2], p[0][3]);
     pb[2] = (int)pack_bf16x2(p[1][0], p[1][1]);
     pb[3] = (int)pack_bf16x2(p[1][2], p[1][3]);
     const bf16x8 pbf = as_bf16x8(pb);
-    // ---- O^T [512 x 16] += Vt . P^T
-    const __bf16* vp = &sm.vt[c16 * kVtPitch + 8 * g];
+    // ---- O^T [512 x 16] += V^T . P^T
+    const unsigned char* vp = tile + tr_base;
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb)
-      o[mb] = mfma16_bf16(as_bf16x8(ld16(vp + 16 * mb * kVtPitch)), pbf, o[mb]);
-    __syncthreads();  // LDS tile is rewritten by the next iteration
+    for (int mb = 0; mb < 32; ++mb) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 32 * mb));
+      const v4i16 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 16 * kPitch + 32 * mb));
+      const i32x2 l2 = __builtin_bit_cast(i32x2, lo);
+      const i32x2 h2 = __builtin_bit_cast(i32x2, hi);
+      const i32x4 av = {l2[0], l2[1], h2[0], h2[1]};
+      o[mb] = mfma16_bf16(as_bf16x8(av), pbf, o[mb]);
+    }
+  };
+
+  // Two buffers with static roles per half-iteration so the compiler can see
+  // that reads of one tile never alias the DMA into the other.
+  // Tiles 0 and 1 are resident; afterwards the DMA of tile n+1 is issued just
+  // before tile n is multiplied and waited for after it.
+  for (int n = 0; n < ntiles; n += 2) {
+    if (n > 0 && n + 1 < ntiles)
+      gather_tile<WAVES>(sm.tile1, kvb, sm.rows + (n + 1) * kRows, lane, wave);
+    compute(sm.tile0, n * kRows);
+    wait_vm_all();
+    __syncthreads();
+    if (n + 1 >= ntiles) break;
+    if (n + 2 < ntiles) gather_tile<WAVES>(sm.tile0, kvb, sm.rows + (n + 2) * kRows, lane, wave);
+    compute(sm.tile1, (n + 1) * kRows);
+    wait_vm_all();
+    __syncthreads();
   }
 
   // ---- finish: total row sum over the four lane groups
@@ -204,8 +253,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
   } else {
     float* pp = part_o + (((int64_t)row * n_split + split) * Hq + head) * kDv + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb)
-      *reinterpret_cast<f32x4*>(pp + 16 * mb) = o[mb] * inv;
+    for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<f32x4*>(pp + 16 * mb) = o[mb] * inv;
     if (g == 0) part_lse[((int64_t)row * n_split + split) * Hq + head] = lse_v;
   }
 }
@@ -241,22 +289,35 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(
     lse[(int64_t)row * Hq + head] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
+#ifndef DSA_ATTN_WG_TARGET
+#define DSA_ATTN_WG_TARGET 512
+#endif
+#ifndef DSA_ATTN_MIN_SPLIT_ROWS
+#define DSA_ATTN_MIN_SPLIT_ROWS 128
+#endif
+
 struct SplitPlan {
   int waves, head_groups, n_split, rows_per_split;
 };
 
+#ifndef DSA_ATTN_MAX_WAVES
+#define DSA_ATTN_MAX_WAVES 4
+#endif
+
 SplitPlan plan_split(int B, int T, int Hq, int k) {
   SplitPlan p;
   const int hb = Hq / 16;
-  p.waves = (hb % 4 == 0) ? 4 : (hb % 2 == 0) ? 2 : 1;
+  p.waves = (hb % 4 == 0 && DSA_ATTN_MAX_WAVES >= 4) ? 4
+            : (hb % 2 == 0 && DSA_ATTN_MAX_WAVES >= 2) ? 2 : 1;
   p.head_groups = hb / p.waves;
   const int base = B * T * p.head_groups;
-  // Enough workgroups to cover the 256 CUs twice, but keep >= 256 rows per
-  // split: every split writes Hq*512 fp32 partials (the size of ~230 rows).
   const int tiles = (k + kRows - 1) / kRows;
-  int ns = (512 + base - 1) / base;
-  ns = max(1, min(ns, tiles / 8));
-  ns = max(1, min(ns, 32));
+  // Enough workgroups to fill the CUs, but every split writes Hq*512 fp32
+  // partials (the size of ~230 gathered rows), so keep splits long.
+  int ns = (DSA_ATTN_WG_TARGET + base - 1) / base;
+  ns = min(ns, max(1, tiles / (DSA_ATTN_MIN_SPLIT_ROWS / kRows)));
+  ns = max(ns, (k + kMaxSplitRows - 1) / kMaxSplitRows);
+  ns = max(1, min(ns, tiles));
   const int tiles_per = (tiles + ns - 1) / ns;
   p.rows_per_split = tiles_per * kRows;
   p.n_split = (k + p.rows_per_split - 1) / p.rows_per_split;
@@ -283,27 +344,21 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
     part_o = reinterpret_cast<float*>(workspace);
     part_lse = part_o + (size_t)B * T * p.n_split * Hq * kDv;
   }
-  const dim3 grid(B * T, p.head_groups, p.n_split);
+  const dim3 grid(B * T * p.head_groups * p.n_split);
   const float sl2 = scale * kLog2e;
   const __bf16* qq = (const __bf16*)q;
   const __bf16* kk = (const __bf16*)kv;
   __bf16* oo = (__bf16*)out;
+#define DSA_ATTN(W)                                                                        \
+  hipLaunchKernelGGL(sparse_mla_kernel<W>, grid, dim3(W * kWave), 0, stream, qq, kk, idx,  \
+                     ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,      \
+                     part_lse, p.n_split, p.head_groups)
   switch (p.waves) {
-    case 4:
-      hipLaunchKernelGGL(sparse_mla_kernel<4>, grid, dim3(4 * kWave), 0, stream, qq, kk, idx,
-                         ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,
-                         part_lse, p.n_split);
-      break;
-    case 2:
-      hipLaunchKernelGGL(sparse_mla_kernel<2>, grid, dim3(2 * kWave), 0, stream, qq, kk, idx,
-                         ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,
-                         part_lse, p.n_split);
-      break;
-    default:
-      hipLaunchKernelGGL(sparse_mla_kernel<1>, grid, dim3(kWave), 0, stream, qq, kk, idx,
-                         ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,
-                         part_lse, p.n_split);
+    case 4: DSA_ATTN(4); break;
+    case 2: DSA_ATTN(2); break;
+    default: DSA_ATTN(1);
   }
+#undef DSA_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
   hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, Hq), dim3(kDv / 4), 0, stream,
