@@ -17,8 +17,8 @@ from typing import Dict, List, Optional, Sequence
 from . import _lib
 from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
 
-__all__ = ["indexer_scores", "topk", "sparse_attn", "run_stack", "DSAError", "library",
-           "ld_for"]
+__all__ = ["indexer_scores", "topk", "topk_workspace_size", "sparse_attn", "run_stack",
+           "Stack", "DSAError", "library", "ld_for"]
 
 
 def library():
@@ -87,11 +87,13 @@ def indexer_scores(q, w, k, ctx_len, q_scale=None, k_scale=None, out=None, strea
     return out[..., :Lmax]
 
 
-def topk(scores, ctx_len, k: int, out=None, stream=None):
+def topk(scores, ctx_len, k: int, out=None, workspace=None, stream=None):
     """Per-row top-k positions, ascending, -1 padded: [B,T,k] int32.
 
     `scores` may be the [B,T,Lmax] view returned by indexer_scores (its row
-    stride is then the padded buffer's)."""
+    stride is then the padded buffer's).  A reused `workspace` (uint8 device
+    tensor of topk_workspace_size bytes) must start zero-filled; calls leave
+    it zero-filled."""
     torch = _torch()
     if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_cuda:
         raise TypeError("scores must be a [B,T,L] float32 device tensor")
@@ -106,10 +108,17 @@ def topk(scores, ctx_len, k: int, out=None, stream=None):
     lib = library()
     need = ctypes.c_size_t(0)
     _lib.check(lib.dsa_topk_workspace_size(B, T, Lmax, k, ctypes.byref(need)))
-    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=scores.device)
+    ws = workspace if workspace is not None else torch.zeros(
+        max(need.value, 1), dtype=torch.uint8, device=scores.device)
     _lib.check(lib.dsa_topk(_ptr(scores), ld, _ptr(ctx_len), B, T, Lmax, k, _ptr(out),
                             _ptr(ws), need.value, _stream(stream)))
     return out
+
+
+def topk_workspace_size(B: int, T: int, Lmax: int, k: int) -> int:
+    need = ctypes.c_size_t(0)
+    _lib.check(library().dsa_topk_workspace_size(B, T, Lmax, k, ctypes.byref(need)))
+    return need.value
 
 
 def sparse_attn(q, kv, idx, ctx_len, scale: float, out=None, lse=None, want_lse=True,
@@ -164,7 +173,7 @@ class Stack:
         _lib.check(library().indexcache_stack_workspace_size(ctypes.byref(self.shape),
                                                              ctypes.byref(need)))
         self.ws_bytes = need.value
-        self.ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(need.value, 1), dtype=torch.uint8, device=dev)
         self.stats = StackStats()
 
     def run(self, stream=None) -> Dict[str, int]:

@@ -131,6 +131,13 @@ dsa_status_t check_attn(const char* fn, const void* q, const void* kv, const int
   return DSA_OK;
 }
 
+// The stack's workspace holds the top-k region (which must stay zero between
+// calls) followed by the attention region.
+size_t topk_region(const dsa_stack_shape_t* s) {
+  const size_t b = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
+  return (b + 255) & ~size_t(255);
+}
+
 dsa_status_t run_indexer(const void* q, dsa_dtype_t dtype, const float* q_scale, const float* w,
                          const void* k, const float* k_scale, const int32_t* ctx_len, int B,
                          int T, int H, int D, int Lmax, float* scores, int64_t ld,
@@ -221,11 +228,10 @@ dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* s, size_t*
   CHECK(s != nullptr && bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: NULL argument", fn);
   CHECK(s->B >= 1 && s->T >= 1 && s->Lmax >= 1 && s->k >= 1, DSA_ERR_INVALID_ARG,
         "%s: bad sizes", fn);
-  size_t need = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
+  size_t need = topk_region(s);
   if (s->Hq > 0) {
     CHECK(s->Hq % 16 == 0 && s->d_v == 512, DSA_ERR_INVALID_ARG, "%s: bad attention sizes", fn);
-    const size_t a = dsa::sparse_attn_workspace_bytes(s->B, s->T, s->Hq, s->k, s->d_v);
-    if (a > need) need = a;
+    need += dsa::sparse_attn_workspace_bytes(s->B, s->T, s->Hq, s->k, s->d_v);
   }
   *bytes = need;
   return ok();
@@ -276,6 +282,8 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
       if (st != DSA_OK) return st;
     }
   }
+  const size_t tk_bytes = topk_region(shape);
+  void* attn_ws = workspace ? static_cast<unsigned char*>(workspace) + tk_bytes : nullptr;
   dsa_stack_stats_t st_local = {0, 0, 0};
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer_t& L = layers[l];
@@ -286,7 +294,7 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
       if (st != DSA_OK) return st;
       st_local.n_indexer_calls++;
       st = hip_status(dsa::launch_topk(score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k,
-                                       idx_buf, workspace, workspace_bytes, stream),
+                                       idx_buf, workspace, tk_bytes, stream),
                       "topk launch");
       if (st != DSA_OK) return st;
       st_local.n_topk_calls++;
@@ -295,7 +303,8 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
     if (s.Hq > 0) {
       dsa_status_t st = hip_status(
           dsa::launch_sparse_attn(L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax, s.k,
-                                  s.scale, L.out, L.lse, workspace, workspace_bytes, stream),
+                                  s.scale, L.out, L.lse, attn_ws, workspace_bytes - tk_bytes,
+                                  stream),
           "sparse attention launch");
       if (st != DSA_OK) return st;
       st_local.n_attn_calls++;

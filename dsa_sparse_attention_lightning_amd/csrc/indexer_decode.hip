@@ -9,14 +9,16 @@
 // with the query resident in registers while key rows stream from HBM:
 //
 //   A = q   [32 heads x D]   (per 32-head block, loaded once per wave)
-//   B = k^T [D x 32 keys]    (one 32-key tile per step, two tiles in flight)
+//   B = k^T [D x 32 keys]    (32-key column blocks of an 8 KB key tile)
 //   C       [32 heads x 32 keys] fp32
 //
-// Lane l supplies key (l & 31) and half (l >> 5) of its D dims, so each lane
-// reads D*e/2 contiguous bytes of one key row.  The epilogue applies ReLU and
-// the per-head weight w' = w (bf16) or w * q_scale (fp8: the positive
-// per-row scales commute with the ReLU) and sums the heads: 16 rows per lane
-// in registers, the other 16 in lane l ^ 32.  Lanes 0..31 then store 32
+// Each wave streams a contiguous run of 8 KB key tiles (64 fp8 or 32 bf16
+// rows of D = 128) with fully coalesced 16-byte loads, three tiles in flight,
+// and regroups each tile through its own LDS region so that lane l holds
+// D*e/2 contiguous bytes of key (l & 31).  The epilogue applies ReLU and the
+// per-head weight w' = w (bf16) or w * q_scale (fp8: the positive per-row
+// scales commute with the ReLU) and sums the heads: 16 rows per lane in
+// registers, the other 16 in lane l ^ 32.  Lanes 0..31 then store 32
 // consecutive fp32 scores (times the key's scale for fp8) or -inf past pos.
 #include "device_common.hpp"
 #include "launchers.hpp"
@@ -25,6 +27,7 @@ namespace dsa {
 namespace {
 
 constexpr int kDecWaves = 4;
+constexpr int kTileBytes = 8192;   // key bytes per wave step
 
 template <int D, bool FP8, int HB>
 __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
@@ -33,10 +36,15 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
     int Lmax, float* __restrict__ scores, int64_t ld, int tiles_per_wave) {
   constexpr int EB = FP8 ? 1 : 2;
-  constexpr int ROWB = D * EB;   // bytes per key row
-  constexpr int HALF = ROWB / 2; // bytes of a row held by one lane
-  constexpr int NV = HALF / 16;  // 16-byte vectors per lane per key
+  constexpr int ROWB = D * EB;            // bytes per key row
+  constexpr int HALF = ROWB / 2;          // bytes of a row held by one lane
+  constexpr int NV = HALF / 16;           // 16-byte vectors per lane per key
+  constexpr int TK = kTileBytes / ROWB;   // keys per tile (8 KB of keys)
+  constexpr int CB = TK / 32;             // 32-key MFMA column blocks per tile
+  constexpr int NL = kTileBytes / 1024;   // 16-byte loads per lane per tile (8)
+  constexpr int PITCH = ROWB + 16;        // LDS row pitch (spreads banks)
   static_assert(NV >= 2 || !FP8, "fp8 needs 32 bytes per lane per MFMA step");
+  __shared__ __align__(16) unsigned char stage[kDecWaves * TK * PITCH];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -45,11 +53,12 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   const int row = blockIdx.y;  // b * T + t
   const int b = row / T;
   const int t = row - b * T;
-  const int tiles = (Lmax + 31) >> 5;
+  const int tiles = (Lmax + TK - 1) / TK;
   const int tile0 = (blockIdx.x * kDecWaves + wave) * tiles_per_wave;
   if (tile0 >= tiles) return;
   const int tend = min(tile0 + tiles_per_wave, tiles);
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
+  unsigned char* my_stage = stage + wave * TK * PITCH;
 
   // Query fragments (operand A) and per-row head weights.
   i32x4 qv[HB][NV];
@@ -72,78 +81,113 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
     }
   }
 
-  const uint8_t* kb = k + (int64_t)b * Lmax * ROWB + g * HALF;
+  const uint8_t* kbase = k + (int64_t)b * Lmax * ROWB;
   const float* ksb = FP8 ? k_scale + (int64_t)b * Lmax : nullptr;
   float* srow = scores + (int64_t)row * ld;
 
-  i32x4 cur[NV], nxt[NV];
-  float cur_s = 1.f, nxt_s = 1.f;
-  {
-    const int key = min(tile0 * 32 + col, Lmax - 1);
+  // A tile is 8 KB of consecutive key rows; lane l loads bytes 16 l + 1024 v
+  // (fully coalesced) and the wave regroups them through its own LDS region
+  // into the MFMA layout, where lane l needs D*e/2 bytes of key (l & 31).
+  // Three register buffers keep tiles t+1 and t+2 in flight while tile t is
+  // multiplied (the loop is unrolled by three so every buffer is static).
+  i32x4 ba[NL], bb[NL], bc[NL];
+  float sa[CB], sb[CB], sc_[CB];
+  auto load = [&](int tile, i32x4(&buf)[NL], float(&bs)[CB]) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) cur[v] = ld16_nt(kb + (int64_t)key * ROWB + 16 * v);
-    if (FP8) cur_s = ksb[key];
-  }
-  for (int tile = tile0; tile < tend; ++tile) {
-    if (tile + 1 < tend) {
-      const int key = min((tile + 1) * 32 + col, Lmax - 1);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) nxt[v] = ld16_nt(kb + (int64_t)key * ROWB + 16 * v);
-      if (FP8) nxt_s = ksb[key];
+    for (int v = 0; v < NL; ++v) {
+      const int off = 16 * lane + 1024 * v;  // byte offset in the tile
+      const int key = min(tile * TK + off / ROWB, Lmax - 1);
+      buf[v] = ld16_nt(kbase + (int64_t)key * ROWB + (off % ROWB));
     }
-    f32x16 acc[HB];
+    if (FP8) {
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16{};
-    if constexpr (!FP8) {
+      for (int c = 0; c < CB; ++c) bs[c] = ksb[min(tile * TK + c * 32 + col, Lmax - 1)];
+    }
+  };
+  auto compute = [&](int tile, const i32x4(&raw)[NL], const float(&cs)[CB]) {
 #pragma unroll
-      for (int s = 0; s < NV; ++s)
+    for (int v = 0; v < NL; ++v) {
+      const int off = 16 * lane + 1024 * v;
+      *reinterpret_cast<i32x4*>(my_stage + (off / ROWB) * PITCH + (off % ROWB)) = raw[v];
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-          acc[hb] = mfma32_bf16(as_bf16x8(qv[hb][s]), as_bf16x8(cur[s]), acc[hb]);
-    } else {
+    for (int c = 0; c < CB; ++c) {
+      i32x4 cur[NV];
 #pragma unroll
-      for (int s = 0; s < NV / 2; ++s) {
-        const i32x8 bk = {cur[2 * s][0], cur[2 * s][1], cur[2 * s][2], cur[2 * s][3],
-                          cur[2 * s + 1][0], cur[2 * s + 1][1], cur[2 * s + 1][2],
-                          cur[2 * s + 1][3]};
+      for (int v = 0; v < NV; ++v)
+        cur[v] = *reinterpret_cast<const i32x4*>(my_stage + (c * 32 + col) * PITCH +
+                                                 g * HALF + 16 * v);
+      f32x16 acc[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          const i32x8 aq = {qv[hb][2 * s][0], qv[hb][2 * s][1], qv[hb][2 * s][2],
-                            qv[hb][2 * s][3], qv[hb][2 * s + 1][0], qv[hb][2 * s + 1][1],
-                            qv[hb][2 * s + 1][2], qv[hb][2 * s + 1][3]};
-          acc[hb] = mfma32_fp8(aq, bk, acc[hb]);
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16{};
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int st = 0; st < NV; ++st)
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+            acc[hb] = mfma32_bf16(as_bf16x8(qv[hb][st]), as_bf16x8(cur[st]), acc[hb]);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NV / 2; ++st) {
+          const i32x8 bk = {cur[2 * st][0], cur[2 * st][1], cur[2 * st][2], cur[2 * st][3],
+                            cur[2 * st + 1][0], cur[2 * st + 1][1], cur[2 * st + 1][2],
+                            cur[2 * st + 1][3]};
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            const i32x8 aq = {qv[hb][2 * st][0], qv[hb][2 * st][1], qv[hb][2 * st][2],
+                              qv[hb][2 * st][3], qv[hb][2 * st + 1][0], qv[hb][2 * st + 1][1],
+                              qv[hb][2 * st + 1][2], qv[hb][2 * st + 1][3]};
+            acc[hb] = mfma32_fp8(aq, bk, acc[hb]);
+          }
         }
       }
+      float sc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc = fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), sc);
+      sc += __shfl_xor(sc, 32, kWave);
+      const int key = tile * TK + c * 32 + col;
+      if (g == 0 && key < Lmax) {
+        float o = -INFINITY;
+        if (key <= pos) o = FP8 ? sc * cs[c] : sc;
+        srow[key] = o;
+      }
     }
-    float sc = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc = fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), sc);
-    sc += __shfl_xor(sc, 32, kWave);
-    const int key = tile * 32 + col;
-    if (g == 0 && key < Lmax) {
-      float o = -INFINITY;
-      if (key <= pos) o = FP8 ? sc * cur_s : sc;
-      srow[key] = o;
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) cur[v] = nxt[v];
-    cur_s = nxt_s;
+    __builtin_amdgcn_wave_barrier();
+  };
+  load(tile0, ba, sa);
+  if (tile0 + 1 < tend) load(tile0 + 1, bb, sb);
+  for (int tile = tile0; tile < tend; tile += 3) {
+    if (tile + 2 < tend) load(tile + 2, bc, sc_);
+    compute(tile, ba, sa);
+    if (tile + 1 >= tend) break;
+    if (tile + 3 < tend) load(tile + 3, ba, sa);
+    compute(tile + 1, bb, sb);
+    if (tile + 2 >= tend) break;
+    if (tile + 4 < tend) load(tile + 4, bb, sb);
+    compute(tile + 2, bc, sc_);
   }
 }
+
+#ifndef DSA_DEC_WG_TARGET
+#define DSA_DEC_WG_TARGET 512
+#endif
 
 template <int D, bool FP8, int HB>
 hipError_t launch_dec(const void* q, const float* q_scale, const float* w, const void* k,
                       const float* k_scale, const int32_t* ctx_len, int B, int T, int H,
                       int Lmax, float* scores, int64_t ld, hipStream_t stream) {
   const int rows = B * T;
-  const int tiles = (Lmax + 31) / 32;
-  // Aim for about 2048 workgroups (8 per CU) so every CU keeps several key
-  // tiles in flight; each wave takes a contiguous run of tiles.
-  int64_t want_waves = 2048LL * kDecWaves;
+  const int tk = kTileBytes / (D * (FP8 ? 1 : 2));
+  const int tiles = (Lmax + tk - 1) / tk;
+  // Few long-lived waves (about 2 workgroups per CU): each takes a long
+  // contiguous run of key tiles, so its query fragments are loaded once and
+  // the DRAM stream of each wave stays sequential.
+  int64_t want_waves = (int64_t)DSA_DEC_WG_TARGET * kDecWaves;
   int tpw = (int)(((int64_t)rows * tiles + want_waves - 1) / want_waves);
-  tpw = max(1, min(tpw, 32));
+  tpw = max(1, min(tpw, 64));
   const int per_block = kDecWaves * tpw;
   dim3 grid((tiles + per_block - 1) / per_block, rows);
   hipLaunchKernelGGL((indexer_decode_kernel<D, FP8, HB>), grid, dim3(kDecWaves * kWave), 0,

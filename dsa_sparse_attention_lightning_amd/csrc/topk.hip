@@ -3,17 +3,28 @@
 //
 // Scores are mapped to order-preserving 32-bit keys and the k-th largest key
 // tau is found by radix selection on 12 + 10 + 10 bits:
-//   pass 1  histogram of the top 12 bits over the visible row      (HBM/L2)
-//   pass 2  ordered copy of every element whose top 12 bits are >= the
-//           threshold bin into an LDS list (keys + positions)       (HBM/L2)
-//   pass 3  two more histogram rounds over the list's threshold-bin
-//           entries give tau and the number of tau-valued elements to keep
-//   pass 4  one ordered scan of the list emits key > tau, plus the first
-//           `take_eq` entries equal to tau (lowest positions first).
+//   1. histogram of the top 12 bits over the visible row -> threshold bin b1
+//      and the count of elements in higher bins;
+//   2. ordered copy of every element whose top 12 bits are >= b1 (a few
+//      thousand for real score rows) into an LDS list (keys + positions);
+//   3. two histogram rounds over the list's b1 entries give tau and the number
+//      of tau-valued elements to keep;
+//   4. one ordered scan of the list emits key > tau, plus the first take_eq
+//      entries equal to tau (lowest positions first).
 // Every compaction is an ordered block-wide prefix sum, so the output comes
 // out in ascending position order and is deterministic.  When the list would
-// overflow LDS (heavily tied rows) passes 3 and 4 re-read the row from
-// memory instead.
+// overflow LDS (heavily tied rows) steps 3 and 4 re-read the row instead.
+//
+// Two launch shapes:
+//   * many rows (prefill): one 1024-thread workgroup per row does 1-4;
+//   * few long rows (decode): each row is cut into chunks; one kernel builds
+//     the step-1 histogram with chunk workgroups (LDS histogram, then global
+//     atomics into a per-row histogram), a second compacts each chunk's
+//     candidates in order into its own slice of a candidate buffer, and a
+//     per-row workgroup concatenates the slices and finishes 3-4.  The
+//     per-row histogram is cleared again by that last kernel, so the
+//     workspace holding it must be zero before the first call and is left
+//     zero by every call.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -25,6 +36,9 @@ constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkCap = 16384;     // LDS list capacity (entries)
 constexpr int kBins1 = 4096;      // top 12 bits
 constexpr int kBins2 = 1024;      // next 10, last 10
+constexpr int kChThreads = 256;   // chunk workgroups
+constexpr int kChWaves = kChThreads / kWave;
+constexpr int kMaxChunks = 256;
 
 struct TopkSmem {
   uint32_t hist[kBins1];
@@ -32,13 +46,14 @@ struct TopkSmem {
   int32_t list_pos[kTkCap];
   uint32_t scan[kTkWaves];
   uint32_t sel[4];
+  uint32_t chunk_off[kMaxChunks + 1];
 };
 
 // Find the bin holding the kk-th largest element (bins scanned from the top):
-// writes {bin, count strictly above it} to sel[0..1].  All threads call.
-template <int NB>
-__device__ void select_bin(const uint32_t* hist, uint32_t kk, TopkSmem& sm) {
-  constexpr int PER = NB / kTkThreads;  // bins per thread (4 or 1)
+// writes {bin, count strictly above it} to sel[0..1].  All NTH threads call.
+template <int NB, int NTH>
+__device__ void select_bin(const uint32_t* hist, uint32_t kk, uint32_t* scan, uint32_t* sel) {
+  constexpr int PER = NB / NTH;  // bins per thread
   const int tid = threadIdx.x;
   uint32_t c[PER];
   uint32_t sum = 0;
@@ -48,12 +63,12 @@ __device__ void select_bin(const uint32_t* hist, uint32_t kk, TopkSmem& sm) {
     sum += c[i];
   }
   uint32_t total;
-  uint32_t above = block_excl_scan<kTkWaves>(sum, sm.scan, total);
+  uint32_t above = block_excl_scan<NTH / kWave>(sum, scan, total);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (above < kk && kk <= above + c[i]) {
-      sm.sel[0] = NB - 1 - (tid * PER + i);
-      sm.sel[1] = above;
+      sel[0] = NB - 1 - (tid * PER + i);
+      sel[1] = above;
     }
     above += c[i];
   }
@@ -109,6 +124,101 @@ __device__ void emit_selected(int count, uint32_t tau, uint32_t take_eq, int32_t
   }
 }
 
+// Steps 3-4 from the LDS list of the M elements in bins >= b1.
+__device__ void finish_from_list(int M, uint32_t b1, uint32_t above1, int k, int32_t* out,
+                                 TopkSmem& sm) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < M; e += kTkThreads) {
+    const uint32_t key = sm.list_key[e];
+    if ((key >> 20) == b1) atomicAdd(&sm.hist[(key >> 10) & 1023u], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1, sm.scan, sm.sel);
+  const uint32_t b2 = sm.sel[0];
+  const uint32_t above2 = sm.sel[1];
+  __syncthreads();
+  const uint32_t pre2 = (b1 << 10) | b2;
+  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < M; e += kTkThreads) {
+    const uint32_t key = sm.list_key[e];
+    if ((key >> 10) == pre2) atomicAdd(&sm.hist[key & 1023u], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1 - above2, sm.scan, sm.sel);
+  const uint32_t b3 = sm.sel[0];
+  const uint32_t above3 = sm.sel[1];
+  __syncthreads();
+  const uint32_t tau = (b1 << 20) | (b2 << 10) | b3;
+  const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
+  emit_selected(M, tau, take_eq, out, sm,
+                [&](int e, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    ok[j] = (e + j) < M;
+                    if (ok[j]) {
+                      key[j] = sm.list_key[e + j];
+                      p[j] = sm.list_pos[e + j];
+                    }
+                  }
+                });
+}
+
+// Steps 3-4 re-reading the row from memory (list would not fit in LDS).
+__device__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t above1, int k,
+                                int32_t* out, TopkSmem& sm) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
+    uint32_t key[4];
+    bool ok[4];
+    load4(src, s, n, key, ok);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (ok[j] && (key[j] >> 20) == b1) atomicAdd(&sm.hist[(key[j] >> 10) & 1023u], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1, sm.scan, sm.sel);
+  const uint32_t b2 = sm.sel[0];
+  const uint32_t above2 = sm.sel[1];
+  __syncthreads();
+  const uint32_t pre2 = (b1 << 10) | b2;
+  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
+    uint32_t key[4];
+    bool ok[4];
+    load4(src, s, n, key, ok);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (ok[j] && (key[j] >> 10) == pre2) atomicAdd(&sm.hist[key[j] & 1023u], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1 - above2, sm.scan, sm.sel);
+  const uint32_t b3 = sm.sel[0];
+  const uint32_t above3 = sm.sel[1];
+  __syncthreads();
+  const uint32_t tau = (b1 << 20) | (b2 << 10) | b3;
+  const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
+  emit_selected(n, tau, take_eq, out, sm,
+                [&](int s, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
+                  load4(src, s, n, key, ok);
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) p[j] = s + j;
+                });
+}
+
+__device__ __forceinline__ int visible(const int32_t* ctx_len, int row, int T, int Lmax) {
+  const int b = row / T;
+  const int t = row - b * T;
+  const int64_t pos = (int64_t)ctx_len[b] - T + t;
+  return (int)max((int64_t)0, min(pos + 1, (int64_t)Lmax));
+}
+
+// ---------------------------------------------------------------- one workgroup per row
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
     int Lmax, int k, int32_t* __restrict__ idx) {
@@ -116,19 +226,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
   TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
-  const int b = row / T;
-  const int t = row - b * T;
-  const int64_t pos = (int64_t)ctx_len[b] - T + t;
-  const int n = (int)max((int64_t)0, min(pos + 1, (int64_t)Lmax));
+  const int n = visible(ctx_len, row, T, Lmax);
   int32_t* out = idx + (int64_t)row * k;
-
   if (n <= k) {  // everything visible is selected
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     return;
   }
   const float* src = scores + (int64_t)row * ld;
-
-  // ---- pass 1: histogram of the top 12 key bits
   for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
   for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
@@ -140,137 +244,256 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
       if (ok[j]) atomicAdd(&sm.hist[key[j] >> 20], 1u);
   }
   __syncthreads();
-  select_bin<kBins1>(sm.hist, (uint32_t)k, sm);
+  select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
   const uint32_t b1 = sm.sel[0];
   const uint32_t above1 = sm.sel[1];
   const uint32_t listed = above1 + sm.hist[b1];
   __syncthreads();
-
-  uint32_t b2, above2, b3, above3;
-  if (listed <= (uint32_t)kTkCap) {
-    // ---- pass 2: ordered copy of elements in bins >= b1 into LDS
-    uint32_t run = 0;
-    for (int base = 0; base < n; base += 4 * kTkThreads) {
-      const int s = base + 4 * tid;
-      uint32_t key[4] = {0, 0, 0, 0};
-      bool ok[4];
-      load4(src, s, n, key, ok);
-      uint32_t c = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ok[j] = ok[j] && (key[j] >> 20) >= b1;
-        c += ok[j];
-      }
-      uint32_t tot;
-      uint32_t at = run + block_excl_scan<kTkWaves>(c, sm.scan, tot);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (ok[j]) {
-          sm.list_key[at] = key[j];
-          sm.list_pos[at] = s + j;
-          ++at;
-        }
-      run += tot;
-    }
-    const int M = (int)listed;
-    // ---- pass 3: refine tau inside the threshold bin
-    for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int e = tid; e < M; e += kTkThreads) {
-      const uint32_t key = sm.list_key[e];
-      if ((key >> 20) == b1) atomicAdd(&sm.hist[(key >> 10) & 1023u], 1u);
-    }
-    __syncthreads();
-    select_bin<kBins2>(sm.hist, (uint32_t)k - above1, sm);
-    b2 = sm.sel[0];
-    above2 = sm.sel[1];
-    __syncthreads();
-    const uint32_t pre2 = (b1 << 10) | b2;
-    for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int e = tid; e < M; e += kTkThreads) {
-      const uint32_t key = sm.list_key[e];
-      if ((key >> 10) == pre2) atomicAdd(&sm.hist[key & 1023u], 1u);
-    }
-    __syncthreads();
-    select_bin<kBins2>(sm.hist, (uint32_t)k - above1 - above2, sm);
-    b3 = sm.sel[0];
-    above3 = sm.sel[1];
-    __syncthreads();
-    const uint32_t tau = (b1 << 20) | (b2 << 10) | b3;
-    const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
-    // ---- pass 4: ordered emission from the list
-    emit_selected(M, tau, take_eq, out, sm,
-                  [&](int e, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                      ok[j] = (e + j) < M;
-                      if (ok[j]) {
-                        key[j] = sm.list_key[e + j];
-                        p[j] = sm.list_pos[e + j];
-                      }
-                    }
-                  });
-  } else {
-    // ---- overflow: the same refinement, reading the row again each pass
-    for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
-      uint32_t key[4];
-      bool ok[4];
-      load4(src, s, n, key, ok);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (ok[j] && (key[j] >> 20) == b1) atomicAdd(&sm.hist[(key[j] >> 10) & 1023u], 1u);
-    }
-    __syncthreads();
-    select_bin<kBins2>(sm.hist, (uint32_t)k - above1, sm);
-    b2 = sm.sel[0];
-    above2 = sm.sel[1];
-    __syncthreads();
-    const uint32_t pre2 = (b1 << 10) | b2;
-    for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
-      uint32_t key[4];
-      bool ok[4];
-      load4(src, s, n, key, ok);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (ok[j] && (key[j] >> 10) == pre2) atomicAdd(&sm.hist[key[j] & 1023u], 1u);
-    }
-    __syncthreads();
-    select_bin<kBins2>(sm.hist, (uint32_t)k - above1 - above2, sm);
-    b3 = sm.sel[0];
-    above3 = sm.sel[1];
-    __syncthreads();
-    const uint32_t tau = (b1 << 20) | (b2 << 10) | b3;
-    const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
-    emit_selected(n, tau, take_eq, out, sm,
-                  [&](int s, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
-                    load4(src, s, n, key, ok);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) p[j] = s + j;
-                  });
+  if (listed > (uint32_t)kTkCap) {
+    finish_from_row(src, n, b1, above1, k, out, sm);
+    return;
   }
+  uint32_t run = 0;
+  for (int base = 0; base < n; base += 4 * kTkThreads) {
+    const int s = base + 4 * tid;
+    uint32_t key[4] = {0, 0, 0, 0};
+    bool ok[4];
+    load4(src, s, n, key, ok);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = ok[j] && (key[j] >> 20) >= b1;
+      c += ok[j];
+    }
+    uint32_t tot;
+    uint32_t at = run + block_excl_scan<kTkWaves>(c, sm.scan, tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (ok[j]) {
+        sm.list_key[at] = key[j];
+        sm.list_pos[at] = s + j;
+        ++at;
+      }
+    run += tot;
+  }
+  finish_from_list((int)listed, b1, above1, k, out, sm);
+}
+
+// ---------------------------------------------------------------- chunked rows
+// Step 1 over one chunk: LDS histogram, then add its non-zero bins to the row's.
+__global__ __launch_bounds__(kChThreads) void topk_chunk_hist_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
+    int Lmax, int k, int chunk, uint32_t* __restrict__ hist_g) {
+  __shared__ uint32_t h[kBins1];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int n = visible(ctx_len, row, T, Lmax);
+  if (n <= k) return;
+  const int c0 = blockIdx.x * chunk;
+  const int c1 = min(n, c0 + chunk);
+  if (c0 >= c1) return;
+  for (int i = tid; i < kBins1; i += kChThreads) h[i] = 0;
+  __syncthreads();
+  const float* src = scores + (int64_t)row * ld;
+  for (int s = c0 + 4 * tid; s < c1; s += 4 * kChThreads) {
+    uint32_t key[4];
+    bool ok[4];
+    load4(src, s, c1, key, ok);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (ok[j]) atomicAdd(&h[key[j] >> 20], 1u);
+  }
+  __syncthreads();
+  uint32_t* hg = hist_g + (int64_t)row * kBins1;
+  for (int i = tid; i < kBins1; i += kChThreads)
+    if (h[i]) atomicAdd(&hg[i], h[i]);
+}
+
+// Step 2 over one chunk: ordered copy of its elements in bins >= b1 into the
+// chunk's own slice [c0, c0 + count) of the row's candidate buffer.
+__global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
+    int Lmax, int k, int chunk, const uint32_t* __restrict__ hist_g,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_pos,
+    uint32_t* __restrict__ cand_cnt, int n_chunks) {
+  __shared__ uint32_t scan[kChWaves];
+  __shared__ uint32_t sel[4];
+  __shared__ uint32_t h[kBins1];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int n = visible(ctx_len, row, T, Lmax);
+  if (n <= k) return;
+  const int c0 = blockIdx.x * chunk;
+  const int c1 = min(n, c0 + chunk);
+  const uint32_t* hg = hist_g + (int64_t)row * kBins1;
+  for (int i = tid; i < kBins1; i += kChThreads) h[i] = hg[i];
+  __syncthreads();
+  select_bin<kBins1, kChThreads>(h, (uint32_t)k, scan, sel);
+  const uint32_t b1 = sel[0];
+  const float* src = scores + (int64_t)row * ld;
+  uint32_t* ck = cand_key + (int64_t)row * Lmax;
+  int32_t* cp = cand_pos + (int64_t)row * Lmax;
+  uint32_t run = 0;
+  for (int base = c0; base < c1; base += 4 * kChThreads) {
+    const int s = base + 4 * tid;
+    uint32_t key[4] = {0, 0, 0, 0};
+    bool ok[4];
+    load4(src, s, c1, key, ok);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = ok[j] && (key[j] >> 20) >= b1;
+      c += ok[j];
+    }
+    uint32_t tot;
+    uint32_t at = run + block_excl_scan<kChWaves>(c, scan, tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (ok[j]) {
+        ck[c0 + at] = key[j];
+        cp[c0 + at] = s + j;
+        ++at;
+      }
+    run += tot;
+  }
+  if (tid == 0) cand_cnt[(int64_t)row * n_chunks + blockIdx.x] = (c0 < c1) ? run : 0u;
+}
+
+// Steps 3-4 for one row from the chunk slices; clears the row's histogram.
+__global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
+    int Lmax, int k, int chunk, int n_chunks, uint32_t* __restrict__ hist_g,
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
+    const uint32_t* __restrict__ cand_cnt, int32_t* __restrict__ idx) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int n = visible(ctx_len, row, T, Lmax);
+  int32_t* out = idx + (int64_t)row * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    return;  // the chunk kernels touched nothing for this row
+  }
+  uint32_t* hg = hist_g + (int64_t)row * kBins1;
+  for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = hg[i];
+  __syncthreads();
+  select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
+  const uint32_t b1 = sm.sel[0];
+  const uint32_t above1 = sm.sel[1];
+  const uint32_t listed = above1 + sm.hist[b1];
+  __syncthreads();
+  for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;  // ready for the next call
+  if (listed > (uint32_t)kTkCap) {
+    finish_from_row(scores + (int64_t)row * ld, n, b1, above1, k, out, sm);
+    return;
+  }
+  // concatenate the chunk slices in chunk order: prefix sum of the slice
+  // counts, then every thread copies entries of the flattened list
+  {
+    const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kTkWaves>(cnt, sm.scan, tot);
+    if (tid < n_chunks) sm.chunk_off[tid] = ex;
+    if (tid == 0) sm.chunk_off[n_chunks] = tot;
+  }
+  __syncthreads();
+  const uint32_t* ck = cand_key + (int64_t)row * Lmax;
+  const int32_t* cp = cand_pos + (int64_t)row * Lmax;
+  for (uint32_t e = tid; e < listed; e += kTkThreads) {
+    int lo = 0, hi = n_chunks - 1;  // last chunk with chunk_off <= e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.chunk_off[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    const int64_t src = (int64_t)lo * chunk + (e - sm.chunk_off[lo]);
+    sm.list_key[e] = ck[src];
+    sm.list_pos[e] = cp[src];
+  }
+  __syncthreads();
+  finish_from_list((int)listed, b1, above1, k, out, sm);
+}
+
+struct TopkPlan {
+  bool chunked;
+  int chunk, n_chunks;
+};
+
+TopkPlan plan_topk(int B, int T, int Lmax) {
+  TopkPlan p{false, 0, 0};
+  const int rows = B * T;
+  if (rows > 128 || Lmax < 16384) return p;
+  // ~512 chunk workgroups, chunks of at least 4096 scores
+  int nc = (512 + rows - 1) / rows;
+  int chunk = (Lmax + nc - 1) / nc;
+  chunk = max(4096, (chunk + 4095) / 4096 * 4096);
+  nc = (Lmax + chunk - 1) / chunk;
+  if (nc > kMaxChunks) return p;
+  p.chunked = true;
+  p.chunk = chunk;
+  p.n_chunks = nc;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct TopkWs {
+  uint32_t* hist;
+  uint32_t* cnt;
+  uint32_t* key;
+  int32_t* pos;
+};
+
+TopkWs carve(void* ws, int rows, int Lmax, int n_chunks) {
+  unsigned char* p = reinterpret_cast<unsigned char*>(ws);
+  TopkWs w;
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * kBins1 * 4);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * n_chunks * 4);
+  w.key = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * Lmax * 4);
+  w.pos = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+hipError_t set_smem_attr(const void* fn, size_t bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int, int, int, int) { return 0; }
+size_t topk_workspace_bytes(int B, int T, int Lmax, int) {
+  const TopkPlan p = plan_topk(B, T, Lmax);
+  if (!p.chunked) return 0;
+  const size_t rows = (size_t)B * T;
+  return align256(rows * kBins1 * 4) + align256(rows * p.n_chunks * 4) +
+         align256(rows * Lmax * 4) + align256(rows * Lmax * 4);
+}
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, int B, int T,
-                       int Lmax, int k, int32_t* idx, void*, size_t, hipStream_t stream) {
-  static bool attr_set = false;
+                       int Lmax, int k, int32_t* idx, void* workspace, size_t,
+                       hipStream_t stream) {
   const size_t smem = sizeof(TopkSmem);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  const TopkPlan p = plan_topk(B, T, Lmax);
+  const int rows = B * T;
+  if (!p.chunked) {
+    hipError_t e = set_smem_attr((const void*)topk_row_kernel, smem);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kTkThreads), smem, stream, scores, ld,
+                       ctx_len, T, Lmax, k, idx);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_row_kernel, dim3(B * T), dim3(kTkThreads), smem, stream, scores, ld,
-                     ctx_len, T, Lmax, k, idx);
+  const TopkWs w = carve(workspace, rows, Lmax, p.n_chunks);
+  const dim3 grid(p.n_chunks, rows);
+  hipLaunchKernelGGL(topk_chunk_hist_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
+                     ctx_len, T, Lmax, k, p.chunk, w.hist);
+  hipLaunchKernelGGL(topk_chunk_collect_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
+                     ctx_len, T, Lmax, k, p.chunk, w.hist, w.key, w.pos, w.cnt, p.n_chunks);
+  hipError_t e = set_smem_attr((const void*)topk_finish_kernel, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kTkThreads), smem, stream, scores, ld,
+                     ctx_len, T, Lmax, k, p.chunk, p.n_chunks, w.hist, w.key, w.pos, w.cnt, idx);
   return hipGetLastError();
 }
 

@@ -93,7 +93,10 @@ dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t dtype, const float* q
  * allowed.
  * scores [B,T,ld_scores] fp32 (only columns 0..pos(b,t) are read),
  * idx    [B,T,k] int32 output.  1 <= k <= 16384, ld_scores multiple of 4.
- * workspace: dsa_topk_workspace_size bytes (may be 0 / NULL when 0).
+ * workspace: dsa_topk_workspace_size bytes (may be 0 / NULL when 0).  Few
+ * long rows are split across workgroups that meet in a per-row histogram
+ * kept in the workspace: the workspace must be zero-filled before its first
+ * use, and every call leaves it zero-filled again.
  */
 dsa_status_t dsa_topk_workspace_size(int B, int T, int Lmax, int k, size_t* bytes);
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx_len, int B,
@@ -163,7 +166,9 @@ typedef struct dsa_stack_stats {
  *   then, if Hq > 0, dsa_sparse_attn(layer l, idx_buf).
  * idx_buf [B,T,k] int32 holds the last F layer's set when the call returns.
  * score_buf [B,T,ld_scores] fp32 scratch, workspace sized by
- * indexcache_stack_workspace_size.  stats (host, may be NULL) receives the
+ * indexcache_stack_workspace_size; like the top-k workspace it must be
+ * zero-filled before its first use and is left that way by every call.
+ * stats (host, may be NULL) receives the
  * number of kernels of each kind that were enqueued.
  */
 dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* shape, size_t* bytes);

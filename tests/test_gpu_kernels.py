@@ -89,6 +89,9 @@ TOPK_CASES = [
     (1, 1, 9000, [9000], 1000, "wide"),
     (1, 12, 4100, [4100], 1024, "normal"),                       # causal rows (T > 1)
     (3, 1, 70, [70, 13, 1], 16, "normal"),
+    (2, 1, 40000, [40000, 39000], 2048, "equal"),                # chunked rows, list overflow
+    (3, 1, 196608, [196608, 100000, 16385], 2048, "normal"),     # chunked, ragged rows
+    (32, 1, 32768, [32768] * 32, 2048, "normal"),                # chunked, many rows
 ]
 
 
@@ -200,3 +203,25 @@ def test_deterministic_reruns():
     b = dsa.indexer_scores(qi.q, qi.w, ki.k, ctx_t, qi.q_scale, ki.k_scale).clone()
     assert torch.equal(a, b)
     assert torch.equal(dsa.topk(a, ctx_t, k), dsa.topk(b, ctx_t, k))
+
+
+def test_topk_workspace_reuse_left_zeroed():
+    """The chunked top-k meets in a per-row histogram inside the workspace: a
+    workspace reused across calls gives the same result as fresh ones and is
+    zero again after each call."""
+    B, T, L, k = 3, 1, 65536, 2048
+    ctx = [65536, 50000, 3000]
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    nbytes = dsa.topk_workspace_size(B, T, L, k)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    for seed in (1, 2, 3):
+        s = _rand_scores(B, T, L, seed=seed)
+        idx = dsa.topk(s, ctx_t, k, workspace=ws)
+        torch.cuda.synchronize()
+        parity.check_topk_exact(idx.cpu().numpy(), s.cpu().numpy(), ctx, k)
+        assert int(ws.count_nonzero().item()) == 0 or _hist_zero(ws, B)
+
+
+def _hist_zero(ws, rows):
+    return int(ws[: rows * 4096 * 4].count_nonzero().item()) == 0
