@@ -8,9 +8,9 @@
 // bytes, so both products run on MFMA (16x16x32 bf16) with an fp32
 // online-softmax accumulator.
 //
-// Work split: a workgroup owns one query row, WAVES*16 heads and one slice of
+// Work split: a workgroup owns one query row, 16*HGW heads and one slice of
 // the k selected rows (split-KV; a combine kernel merges slices by their
-// log-sum-exp).  Each wave owns 16 heads: its query block stays in registers
+// log-sum-exp; slice outputs are kept in bf16 after normalisation).  Each wave owns 16 heads: its query block stays in registers
 // (operand B of S^T = K . q^T) and its O^T accumulator [512 x 16] is 128 fp32
 // per lane.  Rows are processed 32 at a time:
 //   * the 32 selected rows are gathered straight from HBM into LDS with
@@ -44,6 +44,7 @@ constexpr int kTileSlots = kRows * kPitchChunks;                  // 2336
 constexpr int kTileLoads = (kTileSlots + kWave - 1) / kWave;      // 37 wave-loads
 constexpr int kTileBytes = kTileLoads * kWave * 16;               // 37888 (with slack)
 constexpr int kMaxSplitRows = 1024;
+constexpr int kOutPitch = 528;            // LDS pitch of a staged 256-dim bf16 output row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;   // log2 headroom of the lazy softmax rescale
@@ -54,10 +55,11 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
 
-template <int WAVES>
-struct AttnSmem {
+template <int HGW>
+struct AttnSmem {  // tile0 and tile1 are adjacent: the output staging spans both
   __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
   __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
+  f32x4 xs[HGW][2][2][kWave];   // partial S^T exchange: [head group][half][mb][lane]
   int32_t rows[kMaxSplitRows];
 };
 
@@ -65,10 +67,10 @@ struct AttnSmem {
 // tile are written in order, 64 per wave instruction; slot p holds chunk
 // p % 73 of row p / 73.  The pad slot of each row and the slack after the
 // last row receive a harmless copy of chunk 0 of the row.
-template <int WAVES>
+template <int NW>
 __device__ __forceinline__ void gather_tile(unsigned char* tile, const __bf16* kvb,
                                             const int32_t* rows, int lane, int wave) {
-  for (int i = wave; i < kTileLoads; i += WAVES) {
+  for (int i = wave; i < kTileLoads; i += NW) {
     const int p = i * kWave + lane;
     int r = p / kPitchChunks;
     int c = p - r * kPitchChunks;
@@ -82,21 +84,58 @@ __device__ __forceinline__ void gather_tile(unsigned char* tile, const __bf16* k
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
+// Workgroup barrier for LDS-only exchanges: this wave's LDS writes are
+// complete before the barrier, but in-flight global loads (the LDS-DMA of the
+// next tile) are not waited for, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight transposing LDS reads (4 MFMA operands: rows +0 and +16 of value
+// blocks mb .. mb+3) issued back to back; the block waits for its own results
+// before returning them.  Written out so the compiler does not hold them
+// behind the in-flight LDS-DMA of the other tile buffer.
+__device__ __forceinline__ void tr_read8(const unsigned char* lds_addr, i32x2_t (&r)[8]) {
+  const uint32_t a = (uint32_t)(uintptr_t)lds_addr;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:18688\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:18720\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:18752\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:18784\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]),
+        "=v"(r[7])
+      : "v"(a)
+      : "memory");
+}
+
+// HGW head groups of 16 heads per workgroup, two waves per group.  Wave
+// (hg, h) computes the partial S^T over latent dims [288 h, 288 h + 288),
+// the pair exchanges partials through LDS, both apply the same online
+// softmax, and wave h accumulates O^T for value dims [256 h, 256 h + 256).
+template <int HGW>
+__global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ ctx_len, int T, int Hq, int Lmax, int k, int rows_per_split,
     float scale_log2, __bf16* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups) {
-  constexpr int NT = WAVES * kWave;
-  __shared__ AttnSmem<WAVES> sm;
+    __bf16* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups) {
+  constexpr int NW = HGW * 2;
+  constexpr int NT = NW * kWave;
+  __shared__ AttnSmem<HGW> sm;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int hg = wave >> 1;      // head group inside the workgroup
+  const int h = wave & 1;        // which half of the dims this wave owns
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  // blockIdx.x -> (row, head group, split); the splits of one (row, head
-  // group) are spread so consecutive workgroups land on different XCDs.
+  // blockIdx.x -> (row, head group of the grid, split)
   const int bid = blockIdx.x;
   const int split = bid % n_split;
   const int rg = bid / n_split;
@@ -104,7 +143,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
   const int row = rg / head_groups;  // b * T + t
   const int b = row / T;
   const int t = row - b * T;
-  const int head = hgi * (WAVES * 16) + wave * 16 + c16;
+  const int head = (hgi * HGW + hg) * 16 + c16;
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   const int j0 = split * rows_per_split;
   const int nrows = max(0, min(k, j0 + rows_per_split) - j0);
@@ -117,49 +156,62 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
     if (v < 0 || (int64_t)v > pos || v >= Lmax) v = -1;
     sm.rows[j] = v;
   }
-  // Query fragments: operand B of S^T (column = head, reduction = dims);
-  // lane group g covers dims [144 g, 144 g + 144).
-  bf16x8 qf[18];
-  {
-    const __bf16* qp = q + ((int64_t)row * Hq + head) * kDqk + 144 * g;
-#pragma unroll
-    for (int i = 0; i < 18; ++i) qf[i] = as_bf16x8(ld16(qp + 8 * i));
-  }
-  f32x4 o[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  const __bf16* kvb = kv + (int64_t)b * Lmax * kDqk;
   __syncthreads();
-
+  const __bf16* kvb = kv + (int64_t)b * Lmax * kDqk;
   // The first two tiles are requested together: a slice of 64 rows (the
   // common decode case) then waits on a single round trip to HBM.
-  if (ntiles > 0) gather_tile<WAVES>(sm.tile0, kvb, sm.rows, lane, wave);
-  if (ntiles > 1) gather_tile<WAVES>(sm.tile1, kvb, sm.rows + kRows, lane, wave);
+  if (ntiles > 0) gather_tile<NW>(sm.tile0, kvb, sm.rows, lane, wave);
+  if (ntiles > 1) gather_tile<NW>(sm.tile1, kvb, sm.rows + kRows, lane, wave);
+
+  // Query fragments for this wave's half of the latent dims: operand B of
+  // S^T (column = head, reduction = dims); lane group g covers dims
+  // [288 h + 72 g, 288 h + 72 g + 72).
+  bf16x8 qf[9];
+  {
+    const __bf16* qp = q + ((int64_t)row * Hq + head) * kDqk + 288 * h + 72 * g;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) qf[i] = as_bf16x8(ld16(qp + 8 * i));
+  }
+  f32x4 o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
   wait_vm_all();
   __syncthreads();
 
   // Per-lane LDS byte offsets that do not depend on the tile.
-  // S^T operand A: row (16 mb + c16), dims 144 g + 8 i.
+  // S^T operand A: row (16 mb + c16), dims 288 h + 72 g + 8 i.
   // O^T operand A (transposing reads): source row 4g + (c16 >> 2) (+16),
-  // dims 16 mb + 4 (c16 & 3).
-  const int qk_base = c16 * kPitch + 288 * g;
-  const int tr_base = (4 * g + (c16 >> 2)) * kPitch + 8 * (c16 & 3);
+  // dims 256 h + 16 mb + 4 (c16 & 3).
+  const int qk_base = c16 * kPitch + 576 * h + 144 * g;
+  const int tr_base = (4 * g + (c16 >> 2)) * kPitch + 512 * h + 8 * (c16 & 3);
+  f32x4* xs_mine = sm.xs[hg][h][0];
+  const f32x4* xs_other = sm.xs[hg][h ^ 1][0];
 
   auto compute = [&](const unsigned char* tile, int tbase) {
-    // ---- S^T [32 rows x 16 heads]
-    f32x4 s[2];
+    // ---- partial S^T [32 rows x 16 heads] over this wave's dims
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const unsigned char* ap = tile + qk_base;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const unsigned char* ap = tile + qk_base + 16 * mb * kPitch;
-#pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * i));
-        acc = mfma16_bf16(a, qf[i], acc);
+      for (int i = 0; i < 9; ++i) {
+        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * i));
+        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * kPitch + 16 * i));
+        s0 = mfma16_bf16(a0, qf[i], s0);
+        s1 = mfma16_bf16(a1, qf[i], s1);
       }
-      s[mb] = acc;
     }
+    xs_mine[lane] = s0;
+    xs_mine[kWave + lane] = s1;
+    lds_barrier();
+    {
+      const f32x4 t0 = xs_other[lane];
+      const f32x4 t1 = xs_other[kWave + lane];
+      // both waves of the pair form the same sum in the same order
+      s0 = h ? (t0 + s0) : (s0 + t0);
+      s1 = h ? (t1 + s1) : (s1 + t1);
+    }
+    f32x4 s[2] = {s0, s1};
     // ---- online softmax (log2 domain); lane holds rows 4g+r and 16+4g+r
     float mt = -INFINITY;
 #pragma unroll
@@ -175,14 +227,14 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
     // Lazy rescaling: the reference max m_run only moves when a tile's max
     // exceeds it by more than 2^kLazy.  P = 2^(s - m_run) then stays below
     // 2^kLazy, and O, l and the log-sum-exp all use the same reference, so the
-    // result is the exact softmax; the O rescale (128 accumulators) runs only
-    // when some head's reference moves, which is rare after the first tile.
+    // result is the exact softmax; the O rescale runs only when some head's
+    // reference moves, which is rare after the first tile.
     const bool need = mt > m_run + kLazy;
     if (__any(need)) {
       const float m_new = need ? mt : m_run;
       const float alpha = need ? exp2f(m_run - m_new) : 1.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
+      for (int i = 0; i < 16; ++i) o[i] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
@@ -202,32 +254,31 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
     pb[2] = (int)pack_bf16x2(p[1][0], p[1][1]);
     pb[3] = (int)pack_bf16x2(p[1][2], p[1][3]);
     const bf16x8 pbf = as_bf16x8(pb);
-    // ---- O^T [512 x 16] += V^T . P^T
+    // ---- O^T [256 x 16] += V^T . P^T for this wave's value dims
     const unsigned char* vp = tile + tr_base;
+    static_assert(16 * kPitch == 18688, "tr_read8 offsets assume a 1168-byte pitch");
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 32 * mb));
-      const v4i16 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 16 * kPitch + 32 * mb));
-      const i32x2 l2 = __builtin_bit_cast(i32x2, lo);
-      const i32x2 h2 = __builtin_bit_cast(i32x2, hi);
-      const i32x4 av = {l2[0], l2[1], h2[0], h2[1]};
-      o[mb] = mfma16_bf16(as_bf16x8(av), pbf, o[mb]);
+    for (int mb = 0; mb < 16; mb += 4) {
+      i32x2_t r[8];
+      tr_read8(vp + 32 * mb, r);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const i32x4 av = {r[2 * j][0], r[2 * j][1], r[2 * j + 1][0], r[2 * j + 1][1]};
+        o[mb + j] = mfma16_bf16(as_bf16x8(av), pbf, o[mb + j]);
+      }
     }
   };
 
-  // Two buffers with static roles per half-iteration so the compiler can see
-  // that reads of one tile never alias the DMA into the other.
   // Tiles 0 and 1 are resident; afterwards the DMA of tile n+1 is issued just
   // before tile n is multiplied and waited for after it.
   for (int n = 0; n < ntiles; n += 2) {
     if (n > 0 && n + 1 < ntiles)
-      gather_tile<WAVES>(sm.tile1, kvb, sm.rows + (n + 1) * kRows, lane, wave);
+      gather_tile<NW>(sm.tile1, kvb, sm.rows + (n + 1) * kRows, lane, wave);
     compute(sm.tile0, n * kRows);
     wait_vm_all();
     __syncthreads();
     if (n + 1 >= ntiles) break;
-    if (n + 2 < ntiles) gather_tile<WAVES>(sm.tile0, kvb, sm.rows + (n + 2) * kRows, lane, wave);
+    if (n + 2 < ntiles) gather_tile<NW>(sm.tile0, kvb, sm.rows + (n + 2) * kRows, lane, wave);
     compute(sm.tile1, (n + 1) * kRows);
     wait_vm_all();
     __syncthreads();
@@ -239,77 +290,108 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_kernel(
   l_tot += __shfl_xor(l_tot, 32, kWave);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   const float lse_v = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  // lane holds O^T[dim = 16 mb + 4 g + r][head]
-  if (n_split == 1) {
-    __bf16* op = out + ((int64_t)row * Hq + head) * kDv + 4 * g;
+  // lane holds O^T[dim = 256 h + 16 mb + 4 g + r][head].  The wave's
+  // [16 heads x 256 dims] bf16 block is staged in LDS (the tile buffers are
+  // free now; rows padded to 528 bytes) and written out as contiguous rows:
+  // a normalised partial (split-KV) or the final output.
+  static_assert(2 * HGW * 16 * kOutPitch <= 2 * kTileBytes, "output staging fits the tiles");
+  unsigned char* st = reinterpret_cast<unsigned char*>(&sm) + wave * (16 * kOutPitch);
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      uint2 pk;
-      pk.x = pack_bf16x2(o[mb][0] * inv, o[mb][1] * inv);
-      pk.y = pack_bf16x2(o[mb][2] * inv, o[mb][3] * inv);
-      *reinterpret_cast<uint2*>(op + 16 * mb) = pk;
+  for (int mb = 0; mb < 16; ++mb) {
+    uint2 pk;
+    pk.x = pack_bf16x2(o[mb][0] * inv, o[mb][1] * inv);
+    pk.y = pack_bf16x2(o[mb][2] * inv, o[mb][3] * inv);
+    *reinterpret_cast<uint2*>(st + c16 * kOutPitch + 32 * mb + 8 * g) = pk;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __bf16* dst = (n_split == 1)
+                    ? out + ((int64_t)row * Hq + head - c16) * kDv
+                    : part_o + (((int64_t)row * n_split + split) * Hq + head - c16) * kDv;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int hr = 2 * i + (lane >> 5);  // head row inside the wave's block
+    const int cb = 16 * (lane & 31);     // byte inside the row's 512
+    const i32x4 v = *reinterpret_cast<const i32x4*>(st + hr * kOutPitch + cb);
+    *reinterpret_cast<i32x4*>(dst + (int64_t)hr * kDv + 256 * h + cb / 2) = v;
+  }
+  if (g == 0 && h == 0) {
+    if (n_split == 1) {
+      if (lse != nullptr) lse[(int64_t)row * Hq + head] = lse_v;
+    } else {
+      part_lse[((int64_t)row * n_split + split) * Hq + head] = lse_v;
     }
-    if (lse != nullptr && g == 0) lse[(int64_t)row * Hq + head] = lse_v;
-  } else {
-    float* pp = part_o + (((int64_t)row * n_split + split) * Hq + head) * kDv + 4 * g;
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<f32x4*>(pp + 16 * mb) = o[mb] * inv;
-    if (g == 0) part_lse[((int64_t)row * n_split + split) * Hq + head] = lse_v;
   }
 }
 
 // Merge split-KV partials: out = sum_i exp(lse_i - lse) * o_i, lse = log sum exp(lse_i).
-__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, int Hq, int n_split,
+// One workgroup per (query row, 8 heads); a thread owns 8 dims of one head
+// and issues the loads of up to kCombUnroll splits before using them.
+constexpr int kCombHeads = 2;
+constexpr int kCombUnroll = 8;
+__global__ __launch_bounds__(kCombHeads * 64) void sparse_mla_combine_kernel(
+    const __bf16* __restrict__ part_o, const float* __restrict__ part_lse, int Hq, int n_split,
     __bf16* __restrict__ out, float* __restrict__ lse) {
   const int row = blockIdx.x;
-  const int head = blockIdx.y;
-  const int d = threadIdx.x * 4;
+  const int head = blockIdx.y * kCombHeads + threadIdx.x / 64;
+  const int d = (threadIdx.x & 63) * 8;
+  if (head >= Hq) return;
   const float* pl = part_lse + (int64_t)row * n_split * Hq + head;
   float mx = -INFINITY;
   for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, pl[(int64_t)i * Hq]);
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (mx != -INFINITY) {
-    for (int i = 0; i < n_split; ++i) {
-      const float li = pl[(int64_t)i * Hq];
-      const float wi = (li == -INFINITY) ? 0.f : expf(li - mx);
-      den += wi;
-      const float4 v = *reinterpret_cast<const float4*>(
-          part_o + (((int64_t)row * n_split + i) * Hq + head) * kDv + d);
-      acc.x += wi * v.x; acc.y += wi * v.y; acc.z += wi * v.z; acc.w += wi * v.w;
+    const __bf16* po = part_o + ((int64_t)row * n_split * Hq + head) * kDv + d;
+    for (int i0 = 0; i0 < n_split; i0 += kCombUnroll) {
+      i32x4 v[kCombUnroll];
+      float wi[kCombUnroll];
+#pragma unroll
+      for (int u = 0; u < kCombUnroll; ++u) {
+        const int i = min(i0 + u, n_split - 1);
+        v[u] = ld16(po + (int64_t)i * Hq * kDv);
+        const float li = pl[(int64_t)i * Hq];
+        wi[u] = (i0 + u < n_split && li != -INFINITY) ? expf(li - mx) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kCombUnroll; ++u) {
+        den += wi[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = (uint32_t)v[u][e];
+          acc[2 * e] += wi[u] * __uint_as_float(x << 16);
+          acc[2 * e + 1] += wi[u] * __uint_as_float(x & 0xFFFF0000u);
+        }
+      }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint2 pk;
-  pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-  pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(out + ((int64_t)row * Hq + head) * kDv + d) = pk;
-  if (lse != nullptr && threadIdx.x == 0)
+  i32x4 pk;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pk[e] = (int)pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<i32x4*>(out + ((int64_t)row * Hq + head) * kDv + d) = pk;
+  if (lse != nullptr && (threadIdx.x & 63) == 0)
     lse[(int64_t)row * Hq + head] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
 #ifndef DSA_ATTN_WG_TARGET
-#define DSA_ATTN_WG_TARGET 512
+#define DSA_ATTN_WG_TARGET 256
 #endif
 #ifndef DSA_ATTN_MIN_SPLIT_ROWS
 #define DSA_ATTN_MIN_SPLIT_ROWS 128
 #endif
+#ifndef DSA_ATTN_MAX_HGW
+#define DSA_ATTN_MAX_HGW 4
+#endif
 
 struct SplitPlan {
-  int waves, head_groups, n_split, rows_per_split;
+  int hgw, head_groups, n_split, rows_per_split;
 };
-
-#ifndef DSA_ATTN_MAX_WAVES
-#define DSA_ATTN_MAX_WAVES 4
-#endif
 
 SplitPlan plan_split(int B, int T, int Hq, int k) {
   SplitPlan p;
   const int hb = Hq / 16;
-  p.waves = (hb % 4 == 0 && DSA_ATTN_MAX_WAVES >= 4) ? 4
-            : (hb % 2 == 0 && DSA_ATTN_MAX_WAVES >= 2) ? 2 : 1;
-  p.head_groups = hb / p.waves;
+  p.hgw = (hb % 4 == 0 && DSA_ATTN_MAX_HGW >= 4) ? 4 : (hb % 2 == 0 && DSA_ATTN_MAX_HGW >= 2) ? 2 : 1;
+  p.head_groups = hb / p.hgw;
   const int base = B * T * p.head_groups;
   const int tiles = (k + kRows - 1) / kRows;
   // Enough workgroups to fill the CUs, but every split writes Hq*512 fp32
@@ -330,7 +412,7 @@ size_t sparse_attn_workspace_bytes(int B, int T, int Hq, int k, int d_v) {
   const SplitPlan p = plan_split(B, T, Hq, k);
   if (p.n_split <= 1) return 0;
   const size_t rows = (size_t)B * T * p.n_split * Hq;
-  return rows * (size_t)d_v * sizeof(float) + rows * sizeof(float) + 256;
+  return rows * (size_t)d_v * 2 + rows * sizeof(float) + 256;
 }
 
 hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
@@ -338,22 +420,22 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                               float scale, void* out, float* lse, void* workspace,
                               size_t ws_bytes, hipStream_t stream) {
   const SplitPlan p = plan_split(B, T, Hq, k);
-  float* part_o = nullptr;
+  __bf16* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.n_split > 1) {
-    part_o = reinterpret_cast<float*>(workspace);
-    part_lse = part_o + (size_t)B * T * p.n_split * Hq * kDv;
+    part_o = reinterpret_cast<__bf16*>(workspace);
+    part_lse = reinterpret_cast<float*>(part_o + (size_t)B * T * p.n_split * Hq * kDv);
   }
   const dim3 grid(B * T * p.head_groups * p.n_split);
   const float sl2 = scale * kLog2e;
   const __bf16* qq = (const __bf16*)q;
   const __bf16* kk = (const __bf16*)kv;
   __bf16* oo = (__bf16*)out;
-#define DSA_ATTN(W)                                                                        \
-  hipLaunchKernelGGL(sparse_mla_kernel<W>, grid, dim3(W * kWave), 0, stream, qq, kk, idx,  \
-                     ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,      \
+#define DSA_ATTN(W)                                                                          \
+  hipLaunchKernelGGL(sparse_mla_kernel<W>, grid, dim3(W * 2 * kWave), 0, stream, qq, kk, idx, \
+                     ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,         \
                      part_lse, p.n_split, p.head_groups)
-  switch (p.waves) {
+  switch (p.hgw) {
     case 4: DSA_ATTN(4); break;
     case 2: DSA_ATTN(2); break;
     default: DSA_ATTN(1);
@@ -361,8 +443,8 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
 #undef DSA_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
-  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, Hq), dim3(kDv / 4), 0, stream,
-                     part_o, part_lse, Hq, p.n_split, oo, lse);
+  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, (Hq + kCombHeads - 1) / kCombHeads),
+                     dim3(kCombHeads * 64), 0, stream, part_o, part_lse, Hq, p.n_split, oo, lse);
   return hipGetLastError();
 }
 
