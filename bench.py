@@ -152,11 +152,17 @@ def decode_bench(args, dev):
                            L["k_idx_scale"], out=score)
 
     t_idx = event_time_ms(run_idx, reps)
-    t_topk = event_time_ms(lambda i=0: dsa.topk(score[..., :s.Lmax], ctx, s.k, out=idx), reps)
+    tk_ws = torch.zeros(max(1, dsa.topk_workspace_size(s.B, s.T, s.Lmax, s.k)),
+                        dtype=torch.uint8, device=dev)
+    t_topk = event_time_ms(lambda i=0: dsa.topk(score[..., :s.Lmax], ctx, s.k, out=idx,
+                                                workspace=tk_ws), reps)
+    at_ws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(s.B, s.T, s.Hq, s.k)),
+                        dtype=torch.uint8, device=dev)
 
     def run_attn(i=0):
         L = layers[i % s.n_layers]
-        dsa.sparse_attn(L["q"], L["kv"], idx, ctx, s.scale, out=L["out"], lse=L["lse"])
+        dsa.sparse_attn(L["q"], L["kv"], idx, ctx, s.scale, out=L["out"], lse=L["lse"],
+                        workspace=at_ws)
 
     t_attn = event_time_ms(run_attn, max(48, reps))
     ib = indexer_bytes(s)

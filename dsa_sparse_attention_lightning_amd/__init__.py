@@ -17,7 +17,8 @@ from typing import Dict, List, Optional, Sequence
 from . import _lib
 from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
 
-__all__ = ["indexer_scores", "topk", "topk_workspace_size", "sparse_attn", "run_stack",
+__all__ = ["indexer_scores", "topk", "topk_workspace_size", "sparse_attn",
+           "sparse_attn_workspace_size", "run_stack",
            "Stack", "DSAError", "library", "ld_for"]
 
 
@@ -121,9 +122,17 @@ def topk_workspace_size(B: int, T: int, Lmax: int, k: int) -> int:
     return need.value
 
 
+def sparse_attn_workspace_size(B: int, T: int, Hq: int, k: int) -> int:
+    need = ctypes.c_size_t(0)
+    _lib.check(library().dsa_sparse_attn_workspace_size(B, T, Hq, k, 512, ctypes.byref(need)))
+    return need.value
+
+
 def sparse_attn(q, kv, idx, ctx_len, scale: float, out=None, lse=None, want_lse=True,
-                stream=None):
-    """Sparse MLA attention: (out [B,T,Hq,512] bf16, lse [B,T,Hq] fp32 or None)."""
+                workspace=None, stream=None):
+    """Sparse MLA attention: (out [B,T,Hq,512] bf16, lse [B,T,Hq] fp32 or None).
+
+    `workspace`: optional uint8 device tensor of sparse_attn_workspace_size bytes."""
     torch = _torch()
     _need(q, "q", (torch.bfloat16,), 4)
     _need(kv, "kv", (torch.bfloat16,), 3)
@@ -140,7 +149,8 @@ def sparse_attn(q, kv, idx, ctx_len, scale: float, out=None, lse=None, want_lse=
     lib = library()
     need = ctypes.c_size_t(0)
     _lib.check(lib.dsa_sparse_attn_workspace_size(B, T, Hq, k, d_v, ctypes.byref(need)))
-    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    ws = workspace if workspace is not None else torch.empty(
+        max(need.value, 1), dtype=torch.uint8, device=q.device)
     _lib.check(lib.dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(idx), _ptr(ctx_len), B, T, Hq, Lmax,
                                    k, d_qk, d_v, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                                    need.value, _stream(stream)))

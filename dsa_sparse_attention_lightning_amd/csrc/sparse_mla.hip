@@ -115,6 +115,52 @@ __device__ __forceinline__ void tr_read8(const unsigned char* lds_addr, i32x2_t 
       : "memory");
 }
 
+// Merge the split-KV partials of one (query row, head, 8 dims) unit:
+// out = sum_i exp(lse_i - lse) * o_i, lse = log sum_i exp(lse_i).
+constexpr int kCombUnroll = 8;
+__device__ __forceinline__ void combine_unit(const __bf16* __restrict__ part_o,
+                                             const float* __restrict__ part_lse, int Hq,
+                                             int n_split, int row, int head, int d,
+                                             __bf16* __restrict__ out, float* __restrict__ lse,
+                                             bool write_lse) {
+  const float* pl = part_lse + (int64_t)row * n_split * Hq + head;
+  float mx = -INFINITY;
+  for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, pl[(int64_t)i * Hq]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (mx != -INFINITY) {
+    const __bf16* po = part_o + ((int64_t)row * n_split * Hq + head) * kDv + d;
+    for (int i0 = 0; i0 < n_split; i0 += kCombUnroll) {
+      i32x4 v[kCombUnroll];
+      float wi[kCombUnroll];
+#pragma unroll
+      for (int u = 0; u < kCombUnroll; ++u) {
+        const int i = min(i0 + u, n_split - 1);
+        v[u] = ld16(po + (int64_t)i * Hq * kDv);
+        const float li = pl[(int64_t)i * Hq];
+        wi[u] = (i0 + u < n_split && li != -INFINITY) ? expf(li - mx) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kCombUnroll; ++u) {
+        den += wi[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = (uint32_t)v[u][e];
+          acc[2 * e] += wi[u] * __uint_as_float(x << 16);
+          acc[2 * e + 1] += wi[u] * __uint_as_float(x & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  i32x4 pk;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pk[e] = (int)pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<i32x4*>(out + ((int64_t)row * Hq + head) * kDv + d) = pk;
+  if (write_lse && lse != nullptr)
+    lse[(int64_t)row * Hq + head] = den > 0.f ? mx + logf(den) : -INFINITY;
+}
+
 // HGW head groups of 16 heads per workgroup, two waves per group.  Wave
 // (hg, h) computes the partial S^T over latent dims [288 h, 288 h + 288),
 // the pair exchanges partials through LDS, both apply the same online
@@ -323,54 +369,16 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
   }
 }
 
-// Merge split-KV partials: out = sum_i exp(lse_i - lse) * o_i, lse = log sum exp(lse_i).
-// One workgroup per (query row, 8 heads); a thread owns 8 dims of one head
-// and issues the loads of up to kCombUnroll splits before using them.
+// Merge split-KV partials.  One workgroup per (query row, 2 heads); a thread
+// owns 8 dims.
 constexpr int kCombHeads = 2;
-constexpr int kCombUnroll = 8;
 __global__ __launch_bounds__(kCombHeads * 64) void sparse_mla_combine_kernel(
     const __bf16* __restrict__ part_o, const float* __restrict__ part_lse, int Hq, int n_split,
     __bf16* __restrict__ out, float* __restrict__ lse) {
-  const int row = blockIdx.x;
   const int head = blockIdx.y * kCombHeads + threadIdx.x / 64;
-  const int d = (threadIdx.x & 63) * 8;
   if (head >= Hq) return;
-  const float* pl = part_lse + (int64_t)row * n_split * Hq + head;
-  float mx = -INFINITY;
-  for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, pl[(int64_t)i * Hq]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (mx != -INFINITY) {
-    const __bf16* po = part_o + ((int64_t)row * n_split * Hq + head) * kDv + d;
-    for (int i0 = 0; i0 < n_split; i0 += kCombUnroll) {
-      i32x4 v[kCombUnroll];
-      float wi[kCombUnroll];
-#pragma unroll
-      for (int u = 0; u < kCombUnroll; ++u) {
-        const int i = min(i0 + u, n_split - 1);
-        v[u] = ld16(po + (int64_t)i * Hq * kDv);
-        const float li = pl[(int64_t)i * Hq];
-        wi[u] = (i0 + u < n_split && li != -INFINITY) ? expf(li - mx) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kCombUnroll; ++u) {
-        den += wi[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = (uint32_t)v[u][e];
-          acc[2 * e] += wi[u] * __uint_as_float(x << 16);
-          acc[2 * e + 1] += wi[u] * __uint_as_float(x & 0xFFFF0000u);
-        }
-      }
-    }
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  i32x4 pk;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) pk[e] = (int)pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-  *reinterpret_cast<i32x4*>(out + ((int64_t)row * Hq + head) * kDv + d) = pk;
-  if (lse != nullptr && (threadIdx.x & 63) == 0)
-    lse[(int64_t)row * Hq + head] = den > 0.f ? mx + logf(den) : -INFINITY;
+  combine_unit(part_o, part_lse, Hq, n_split, blockIdx.x, head, (threadIdx.x & 63) * 8, out,
+               lse, (threadIdx.x & 63) == 0);
 }
 
 #ifndef DSA_ATTN_WG_TARGET
@@ -408,11 +416,35 @@ SplitPlan plan_split(int B, int T, int Hq, int k) {
 
 }  // namespace
 
-size_t sparse_attn_workspace_bytes(int B, int T, int Hq, int k, int d_v) {
+namespace {
+
+size_t part_bytes(const SplitPlan& p, int B, int T, int Hq) {
+  const size_t rows = (size_t)B * T * p.n_split * Hq;
+  return (rows * kDv * 2 + rows * sizeof(float) + 255) & ~size_t(255);
+}
+
+template <int HGW>
+hipError_t launch_attn(const SplitPlan& p, const __bf16* q, const __bf16* kv, const int32_t* idx,
+                       const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k, float sl2,
+                       __bf16* out, float* lse, __bf16* part_o, float* part_lse,
+                       hipStream_t stream) {
+  const dim3 grid(B * T * p.head_groups * p.n_split);
+  hipLaunchKernelGGL((sparse_mla_kernel<HGW>), grid, dim3(HGW * 2 * kWave), 0, stream, q, kv,
+                     idx, ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, out, lse, part_o,
+                     part_lse, p.n_split, p.head_groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split <= 1) return e;
+  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, (Hq + kCombHeads - 1) / kCombHeads),
+                     dim3(kCombHeads * 64), 0, stream, part_o, part_lse, Hq, p.n_split, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t sparse_attn_workspace_bytes(int B, int T, int Hq, int k, int) {
   const SplitPlan p = plan_split(B, T, Hq, k);
   if (p.n_split <= 1) return 0;
-  const size_t rows = (size_t)B * T * p.n_split * Hq;
-  return rows * (size_t)d_v * 2 + rows * sizeof(float) + 256;
+  return part_bytes(p, B, T, Hq);
 }
 
 hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
@@ -426,26 +458,15 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
     part_o = reinterpret_cast<__bf16*>(workspace);
     part_lse = reinterpret_cast<float*>(part_o + (size_t)B * T * p.n_split * Hq * kDv);
   }
-  const dim3 grid(B * T * p.head_groups * p.n_split);
   const float sl2 = scale * kLog2e;
   const __bf16* qq = (const __bf16*)q;
   const __bf16* kk = (const __bf16*)kv;
   __bf16* oo = (__bf16*)out;
-#define DSA_ATTN(W)                                                                          \
-  hipLaunchKernelGGL(sparse_mla_kernel<W>, grid, dim3(W * 2 * kWave), 0, stream, qq, kk, idx, \
-                     ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, oo, lse, part_o,         \
-                     part_lse, p.n_split, p.head_groups)
   switch (p.hgw) {
-    case 4: DSA_ATTN(4); break;
-    case 2: DSA_ATTN(2); break;
-    default: DSA_ATTN(1);
+    case 4: return launch_attn<4>(p, qq, kk, idx, ctx_len, B, T, Hq, Lmax, k, sl2, oo, lse, part_o, part_lse, stream);
+    case 2: return launch_attn<2>(p, qq, kk, idx, ctx_len, B, T, Hq, Lmax, k, sl2, oo, lse, part_o, part_lse, stream);
+    default: return launch_attn<1>(p, qq, kk, idx, ctx_len, B, T, Hq, Lmax, k, sl2, oo, lse, part_o, part_lse, stream);
   }
-#undef DSA_ATTN
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split <= 1) return e;
-  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, (Hq + kCombHeads - 1) / kCombHeads),
-                     dim3(kCombHeads * 64), 0, stream, part_o, part_lse, Hq, p.n_split, oo, lse);
-  return hipGetLastError();
 }
 
 }  // namespace dsa

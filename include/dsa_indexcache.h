@@ -119,6 +119,10 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx
  * out [B,T,Hq,d_v] bf16 (round to nearest even from fp32),
  * lse [B,T,Hq] fp32 or NULL.  Softmax and accumulation are fp32.
  * Supported: d_qk == 576, d_v == 512, Hq a multiple of 16, 1 <= k <= 65536.
+ * workspace: dsa_sparse_attn_workspace_size bytes (may be 0 / NULL when
+ * 0): when the selected rows are split across workgroups it holds the
+ * per-slice outputs (bf16, normalised by their own softmax sums) and their
+ * fp32 log-sum-exp until a combine pass merges them.
  */
 dsa_status_t dsa_sparse_attn_workspace_size(int B, int T, int Hq, int k, int d_v,
                                             size_t* bytes);
