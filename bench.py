@@ -18,7 +18,12 @@ Also reported on the same line:
     same shape in bf16): indexer scores TFLOP/s and top-k time;
   * the fp64 CPU oracle timed on a bounded sample on this host.
 
+  * the pattern sweep at context 196608 (16 layers, batch 4): all-F, FS,
+    FSSS, FSSSSSSS, with the overlap between each S layer's reused index set
+    and the set its own indexer would select.
+
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
+                [--no-sweep]
 """
 from __future__ import annotations
 
@@ -190,6 +195,52 @@ def decode_bench(args, dev):
     return s, layers, res, cut, kernels, roof
 
 
+def pattern_sweep(dev, steps, warmup, cfg=4):
+    """The pattern sweep near maximum context: step time, indexer+top-k time
+    per layer, and the overlap between the index set each S layer reuses and
+    the set its own indexer would have produced (rows and S layers averaged)."""
+    import numpy as np
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    s = gen.CONFIGS[cfg]
+    layers = build_decode_workload(s, dev)
+    ctx = gen.ctx_lens(s, dev)
+    own = []
+    for L in layers:   # each layer's own selection (what an F layer would compute)
+        sc = dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx, L["q_idx_scale"],
+                                L["k_idx_scale"])
+        own.append(dsa.topk(sc, ctx, s.k).cpu().numpy())
+    out = {}
+    for p in s.patterns:
+        st = dsa.Stack(p, layers, ctx, **shape_kw(s))
+        ms, stats = time_stack(st, steps, warmup)
+        st_i = dsa.Stack(p, layers, ctx, **shape_kw(s, attn=False))
+        ms_i, _ = time_stack(st_i, steps, warmup)
+        ovs = []
+        last_f = 0
+        for l, c in enumerate(p):
+            if c == "F":
+                last_f = l
+                continue
+            for b in range(s.B):
+                a, o = own[last_f][b, 0], own[l][b, 0]
+                ovs.append(np.intersect1d(a[a >= 0], o[o >= 0]).size / max(1, (o >= 0).sum()))
+        key = "all-F" if set(p) == {"F"} else next(
+            p[:n] for n in range(1, len(p) + 1) if gen.tile_pattern(p[:n], len(p)) == p)
+        out[key] = dict(ms_per_step=round(ms, 4), tokens_per_s=round(s.B / (ms * 1e-3), 1),
+                        n_indexer_calls=stats["n_indexer_calls"],
+                        indexer_topk_us_per_layer=round(ms_i * 1e3 / s.n_layers, 3),
+                        per_token_latency_ms=round(ms, 4),
+                        reuse_overlap=round(float(np.mean(ovs)), 4) if ovs else None)
+        log(f"sweep {key:9s} {ms:7.3f} ms/step  indexer+topk {ms_i * 1e3 / s.n_layers:7.2f} "
+            f"us/layer  overlap {out[key]['reuse_overlap']}")
+    del layers
+    torch.cuda.empty_cache()
+    return dict(workload=f"{s.name}: {s.n_layers} layers, batch {s.B}, context {s.ctx}",
+                patterns=out)
+
+
 def prefill_bench(dev, reps=5):
     import torch
     import dsa_sparse_attention_lightning_amd as dsa
@@ -279,6 +330,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 196K-context pattern sweep")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -297,6 +349,9 @@ def main():
 
     s, layers, res, cut, kernels, roof = decode_bench(args, dev)
     main_res = res["config"]
+    sweep = None
+    if not args.no_sweep:
+        sweep = pattern_sweep(dev, max(5, args.steps // 3), 2)
     prefill = None if args.no_prefill else prefill_bench(dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -329,6 +384,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "prefill": prefill,
+        "pattern_sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 
