@@ -120,6 +120,27 @@ def attn_bytes_flops(s):
     return s.B * s.T * per_row, s.B * s.T * flops
 
 
+def recorded_traffic(kernel: str, source: str):
+    """HBM bytes per call measured by hardware counters (two rocprofv3 --pmc
+    passes, scaled by a plain copy of known size) as recorded in the
+    committed profile summary - or None once the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "decode_c3_traffic_pmc.md")
+    src = os.path.join(ROOT, "dsa_sparse_attention_lightning_amd", "csrc", source)
+    try:
+        text = open(prof).read()
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(rf"- source-sha256: {re.escape(source)} (\w+)", text)
+    t = re.search(rf"- traffic: {re.escape(kernel)} (\d+)", text)
+    if not m or not t or m.group(1) != cur:
+        return None
+    return int(t.group(1))
+
+
 def decode_bench(args, dev):
     import torch
     import dsa_sparse_attention_lightning_amd as dsa
@@ -189,9 +210,19 @@ def decode_bench(args, dev):
             f"{v['gbs']:8.1f} GB/s")
     dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
     kd = kernels[dom]
+    src = {"indexer_decode": "indexer_decode.hip", "sparse_mla": "sparse_mla.hip",
+           "topk": "topk.hip"}[dom]
     roof = dict(kernel=dom, bound="hbm", achieved=round(kd["gbs"], 1), peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=round(kd["gbs"] / HBM_PEAK_GBS, 4), traffic=None,
+                unit="GB/s", frac=round(kd["gbs"] / HBM_PEAK_GBS, 4),
+                traffic=recorded_traffic(dom, src),
                 per_launch_bytes=kd["bytes"], avg_launch_us=round(kd["us"], 3))
+    if dom == "sparse_mla":
+        roof["mfma_tflops"] = round(kd["tflops"], 1)
+        roof["mfma_frac_bf16"] = round(kd["tflops"] / BF16_PEAK_TFLOPS, 4)
+    for name, v in kernels.items():
+        v["traffic"] = recorded_traffic(name, {"indexer_decode": "indexer_decode.hip",
+                                               "sparse_mla": "sparse_mla.hip",
+                                               "topk": "topk.hip"}[name])
     return s, layers, res, cut, kernels, roof
 
 
@@ -331,6 +362,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 196K-context pattern sweep")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -346,6 +380,12 @@ def main():
     dsa.library()  # fail loudly if the HIP library is missing
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     s, layers, res, cut, kernels, roof = decode_bench(args, dev)
     main_res = res["config"]
