@@ -39,6 +39,8 @@ constexpr int kBins2 = 1024;      // next 10, last 10
 constexpr int kChThreads = 256;   // chunk workgroups
 constexpr int kChWaves = kChThreads / kWave;
 constexpr int kMaxChunks = 256;
+constexpr int kPer = 16;         // scores per thread per chunk batch (4096 per workgroup)
+constexpr int kGather = 8;       // candidate loads in flight per thread
 
 struct TopkSmem {
   uint32_t hist[kBins1];
@@ -295,13 +297,18 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_hist_kernel(
   for (int i = tid; i < kBins1; i += kChThreads) h[i] = 0;
   __syncthreads();
   const float* src = scores + (int64_t)row * ld;
-  for (int s = c0 + 4 * tid; s < c1; s += 4 * kChThreads) {
-    uint32_t key[4];
-    bool ok[4];
-    load4(src, s, c1, key, ok);
+  // a thread owns kPer consecutive scores of each batch; all loads first
+  for (int base = c0; base < c1; base += kPer * kChThreads) {
+    const int s0 = base + kPer * tid;
+    uint32_t key[kPer / 4][4];
+    bool ok[kPer / 4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j]) atomicAdd(&h[key[j] >> 20], 1u);
+    for (int v = 0; v < kPer / 4; ++v) load4(src, s0 + 4 * v, c1, key[v], ok[v]);
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ok[v][j]) atomicAdd(&h[key[v][j] >> 20], 1u);
   }
   __syncthreads();
   uint32_t* hg = hist_g + (int64_t)row * kBins1;
@@ -334,26 +341,31 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
   uint32_t* ck = cand_key + (int64_t)row * Lmax;
   int32_t* cp = cand_pos + (int64_t)row * Lmax;
   uint32_t run = 0;
-  for (int base = c0; base < c1; base += 4 * kChThreads) {
-    const int s = base + 4 * tid;
-    uint32_t key[4] = {0, 0, 0, 0};
-    bool ok[4];
-    load4(src, s, c1, key, ok);
+  for (int base = c0; base < c1; base += kPer * kChThreads) {
+    const int s0 = base + kPer * tid;
+    uint32_t key[kPer / 4][4];
+    bool ok[kPer / 4][4];
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v) load4(src, s0 + 4 * v, c1, key[v], ok[v]);
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ok[j] = ok[j] && (key[j] >> 20) >= b1;
-      c += ok[j];
-    }
+    for (int v = 0; v < kPer / 4; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[v][j] = ok[v][j] && (key[v][j] >> 20) >= b1;
+        c += ok[v][j];
+      }
     uint32_t tot;
     uint32_t at = run + block_excl_scan<kChWaves>(c, scan, tot);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j]) {
-        ck[c0 + at] = key[j];
-        cp[c0 + at] = s + j;
-        ++at;
-      }
+    for (int v = 0; v < kPer / 4; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ok[v][j]) {
+          ck[c0 + at] = key[v][j];
+          cp[c0 + at] = s0 + 4 * v + j;
+          ++at;
+        }
     run += tot;
   }
   if (tid == 0) cand_cnt[(int64_t)row * n_chunks + blockIdx.x] = (c0 < c1) ? run : 0u;
@@ -400,15 +412,33 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   __syncthreads();
   const uint32_t* ck = cand_key + (int64_t)row * Lmax;
   const int32_t* cp = cand_pos + (int64_t)row * Lmax;
-  for (uint32_t e = tid; e < listed; e += kTkThreads) {
-    int lo = 0, hi = n_chunks - 1;  // last chunk with chunk_off <= e
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.chunk_off[mid] <= e) lo = mid; else hi = mid - 1;
+  // gather in batches of kGather entries per thread, all loads issued first
+  for (uint32_t e0 = 0; e0 < listed; e0 += kGather * kTkThreads) {
+    uint32_t kv[kGather];
+    int32_t pv[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const uint32_t e = e0 + u * kTkThreads + tid;
+      int64_t at = 0;
+      if (e < listed) {
+        int lo = 0, hi = n_chunks - 1;  // last chunk with chunk_off <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.chunk_off[mid] <= e) lo = mid; else hi = mid - 1;
+        }
+        at = (int64_t)lo * chunk + (e - sm.chunk_off[lo]);
+      }
+      kv[u] = ck[at];
+      pv[u] = cp[at];
     }
-    const int64_t src = (int64_t)lo * chunk + (e - sm.chunk_off[lo]);
-    sm.list_key[e] = ck[src];
-    sm.list_pos[e] = cp[src];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const uint32_t e = e0 + u * kTkThreads + tid;
+      if (e < listed) {
+        sm.list_key[e] = kv[u];
+        sm.list_pos[e] = pv[u];
+      }
+    }
   }
   __syncthreads();
   finish_from_list((int)listed, b1, above1, k, out, sm);
