@@ -48,41 +48,33 @@ constexpr int kOutPitch = 528;            // LDS pitch of a staged 256-dim bf16 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;   // log2 headroom of the lazy softmax rescale
+#ifndef DSA_ATTN_XCD
+#define DSA_ATTN_XCD 1
+#endif
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 
 
-template <int HGW>
-struct AttnSmem {  // tile0 and tile1 are adjacent: the output staging spans both
-  __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
-  __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
-  f32x4 xs[HGW][2][2][kWave];   // partial S^T exchange: [head group][half][mb][lane]
-  int32_t rows[kMaxSplitRows];
-};
-
-// Issue the LDS-DMA gather of one 32-row tile: the 16-byte LDS slots of the
-// tile are written in order, 64 per wave instruction; slot p holds chunk
-// p % 73 of row p / 73.  The pad slot of each row and the slack after the
-// last row receive a harmless copy of chunk 0 of the row.
-template <int NW>
-__device__ __forceinline__ void gather_tile(unsigned char* tile, const __bf16* kvb,
-                                            const int32_t* rows, int lane, int wave) {
-  for (int i = wave; i < kTileLoads; i += NW) {
-    const int p = i * kWave + lane;
-    int r = p / kPitchChunks;
-    int c = p - r * kPitchChunks;
-    if (c >= kChunks) c = 0;
-    if (r >= kRows) { r = 0; c = 0; }
-    const int src = max(rows[r], 0);
-    __builtin_amdgcn_global_load_lds((const void*)(kvb + (int64_t)src * kDqk + 8 * c),
-                                     (lds_void*)(tile + i * kWave * 16), 16, 0, 0);
-  }
+// Slot of one 16-byte LDS-DMA load inside a tile: instruction i of the tile
+// writes slots 64 i .. 64 i + 63, and slot p holds chunk p % 73 of row p / 73.
+// The pad slot of each row and the slack after the last row receive a
+// harmless copy of chunk 0 of row 0.  Packed as (row << 16) | byte offset.
+__device__ __forceinline__ int gather_slot(int i, int lane) {
+  const int p = i * kWave + lane;
+  int r = p / kPitchChunks;
+  int c = p - r * kPitchChunks;
+  if (c >= kChunks) c = 0;
+  if (r >= kRows) { r = 0; c = 0; }
+  return (r << 16) | (c * 16);
 }
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum), as a
+// builtin so that the compiler's own wait-count tracking sees it.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier for LDS-only exchanges: this wave's LDS writes are
 // complete before the barrier, but in-flight global loads (the LDS-DMA of the
@@ -91,28 +83,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
+// Maximum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
-// Eight transposing LDS reads (4 MFMA operands: rows +0 and +16 of value
-// blocks mb .. mb+3) issued back to back; the block waits for its own results
-// before returning them.  Written out so the compiler does not hold them
-// behind the in-flight LDS-DMA of the other tile buffer.
-__device__ __forceinline__ void tr_read8(const unsigned char* lds_addr, i32x2_t (&r)[8]) {
-  const uint32_t a = (uint32_t)(uintptr_t)lds_addr;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:18688\n\t"
-      "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
-      "ds_read_b64_tr_b16 %3, %8 offset:18720\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
-      "ds_read_b64_tr_b16 %5, %8 offset:18752\n\t"
-      "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
-      "ds_read_b64_tr_b16 %7, %8 offset:18784\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]),
-        "=v"(r[7])
-      : "v"(a)
-      : "memory");
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even, one instruction).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ v4i16 tr_read(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
 }
 
 // Merge the split-KV partials of one (query row, head, 8 dims) unit:
@@ -170,23 +159,44 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ ctx_len, int T, int Hq, int Lmax, int k, int rows_per_split,
     float scale_log2, __bf16* __restrict__ out, float* __restrict__ lse,
-    __bf16* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups) {
+    __bf16* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups,
+    int n_work, int per_xcd) {
   constexpr int NW = HGW * 2;
   constexpr int NT = NW * kWave;
-  __shared__ AttnSmem<HGW> sm;
+  constexpr int KJ = (kTileLoads + NW - 1) / NW;  // DMA instructions per wave per tile
+  // Three tile buffers, as separate LDS objects so that the compiler can tell
+  // that reading one buffer does not depend on the DMA still writing another.
+  // While tile n is multiplied by P, tile n+1 is multiplied by q and tile n+2
+  // streams in.
+  __shared__ __attribute__((aligned(16))) unsigned char tileA[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tileB[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tileC[kTileBytes];
+  __shared__ f32x4 xs[2][HGW][2][2][kWave];  // partial S^T exchange: [tile parity][group][half][mb][lane]
+  __shared__ int32_t rows[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) float bias[kMaxSplitRows];  // 0 or -inf per row
+
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hg = wave >> 1;      // head group inside the workgroup
   const int h = wave & 1;        // which half of the dims this wave owns
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  // blockIdx.x -> (row, head group of the grid, split)
+  // Work item w = ((row * n_split) + split) * head_groups + head group.  The
+  // dispatcher deals consecutive workgroups to the 8 XCDs in turn, so
+  // workgroup i runs on XCD i % 8; giving each XCD one contiguous range of
+  // work items keeps a query row's fragments and the rows its head groups
+  // gather together in one XCD's L2 instead of fetching them 8 times.
+#if DSA_ATTN_XCD
+  const int bid = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+#else
   const int bid = blockIdx.x;
-  const int split = bid % n_split;
-  const int rg = bid / n_split;
-  const int hgi = rg % head_groups;
-  const int row = rg / head_groups;  // b * T + t
+#endif
+  if (bid >= n_work) return;
+  const int hgi = bid % head_groups;
+  const int rs = bid / head_groups;
+  const int split = rs % n_split;
+  const int row = rs / n_split;  // b * T + t
   const int b = row / T;
   const int t = row - b * T;
   const int head = (hgi * HGW + hg) * 16 + c16;
@@ -195,19 +205,40 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
   const int nrows = max(0, min(k, j0 + rows_per_split) - j0);
   const int ntiles = (nrows + kRows - 1) / kRows;
 
-  // Selected rows of this slice, validated once (invalid / padding -> -1).
+  // Selected rows of this slice, validated once (invalid / padding -> -1,
+  // whose score bias is -inf).
   const int32_t* ib = idx + (int64_t)row * k + j0;
   for (int j = tid; j < ntiles * kRows; j += NT) {
     int v = (j < nrows) ? ib[j] : -1;
     if (v < 0 || (int64_t)v > pos || v >= Lmax) v = -1;
-    sm.rows[j] = v;
+    rows[j] = v;
+    bias[j] = v >= 0 ? 0.f : -INFINITY;
   }
+  // This wave's DMA slots are the same for every tile.
+  int gslot[KJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) gslot[j] = gather_slot(wave + NW * j, lane);
   __syncthreads();
-  const __bf16* kvb = kv + (int64_t)b * Lmax * kDqk;
+  const unsigned char* kvb = reinterpret_cast<const unsigned char*>(kv + (int64_t)b * Lmax * kDqk);
+  // Issue the LDS-DMA gather of one 32-row tile: look up the rows of all of
+  // this wave's slots first, then issue the loads back to back (a slot past
+  // the tile's last instruction maps to row 0: its lookup is harmless and its
+  // load is skipped; only the last j can be such a slot).
+  auto gather = [&](unsigned char* tile, int tbase) {
+    int src[KJ];
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) src[j] = rows[tbase + (gslot[j] >> 16)];
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+      if (NW * j + NW - 1 < kTileLoads || wave + NW * j < kTileLoads)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(kvb + (int64_t)max(src[j], 0) * kRowBytes + (gslot[j] & 0xffff)),
+            (lds_void*)(tile + (wave + NW * j) * kWave * 16), 16, 0, 0);
+  };
   // The first two tiles are requested together: a slice of 64 rows (the
   // common decode case) then waits on a single round trip to HBM.
-  if (ntiles > 0) gather_tile<NW>(sm.tile0, kvb, sm.rows, lane, wave);
-  if (ntiles > 1) gather_tile<NW>(sm.tile1, kvb, sm.rows + kRows, lane, wave);
+  if (ntiles > 0) gather(tileA, 0);
+  if (ntiles > 1) gather(tileB, kRows);
 
   // Query fragments for this wave's half of the latent dims: operand B of
   // S^T (column = head, reduction = dims); lane group g covers dims
@@ -218,12 +249,16 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
 #pragma unroll
     for (int i = 0; i < 9; ++i) qf[i] = as_bf16x8(ld16(qp + 8 * i));
   }
+  // The fragments must have arrived before the tile loop starts: otherwise
+  // the compiler may move these loads below the barrier, and the wait for
+  // them then sits at the loop head, where it would also wait for every
+  // tile's DMA.
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
+               "v"(qf[6]), "v"(qf[7]), "v"(qf[8]));
   f32x4 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  wait_vm_all();
-  __syncthreads();
 
   // Per-lane LDS byte offsets that do not depend on the tile.
   // S^T operand A: row (16 mb + c16), dims 288 h + 72 g + 8 i.
@@ -231,45 +266,79 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
   // dims 256 h + 16 mb + 4 (c16 & 3).
   const int qk_base = c16 * kPitch + 576 * h + 144 * g;
   const int tr_base = (4 * g + (c16 >> 2)) * kPitch + 512 * h + 8 * (c16 & 3);
-  f32x4* xs_mine = sm.xs[hg][h][0];
-  const f32x4* xs_other = sm.xs[hg][h ^ 1][0];
 
-  auto compute = [&](const unsigned char* tile, int tbase) {
-    // ---- partial S^T [32 rows x 16 heads] over this wave's dims
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      const unsigned char* ap = tile + qk_base;
+  // Partial S^T [32 rows x 16 heads] of one tile over this wave's dims.
+  auto qk = [&](const unsigned char* tile, f32x4& s0, f32x4& s1) {
+    i32x4 ka[9], kb[9];
+    const unsigned char* ap = tile + qk_base;
 #pragma unroll
-      for (int i = 0; i < 9; ++i) {
-        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * i));
-        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * kPitch + 16 * i));
-        s0 = mfma16_bf16(a0, qf[i], s0);
-        s1 = mfma16_bf16(a1, qf[i], s1);
+    for (int i = 0; i < 9; ++i) {
+      ka[i] = *(const lds_i32x4*)(ap + 16 * i);
+      kb[i] = *(const lds_i32x4*)(ap + 16 * kPitch + 16 * i);
+    }
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      s0 = mfma16_bf16(as_bf16x8(ka[i]), qf[i], s0);
+      s1 = mfma16_bf16(as_bf16x8(kb[i]), qf[i], s1);
+    }
+  };
+
+  f32x4 sp0, sp1;  // this wave's partial S^T of the tile about to be softmaxed
+  if (ntiles > 0) {
+    wait_vm_all();
+    __syncthreads();
+    qk(tileA, sp0, sp1);
+  }
+
+  // One step: softmax and P.V of tile n (buffer P) while S^T of tile n+1
+  // (buffer Q, resident) is formed and tile n+2 streams into buffer D, which
+  // held tile n-1.  One barrier per step: after it, tile n+1 has landed
+  // (every wave waited for its own DMA), the partials of tile n are visible,
+  // and every wave has finished tile n-1, so D may be overwritten.
+  auto step = [&](int n, const unsigned char* P, const unsigned char* Q, unsigned char* D) {
+    const int par = n & 1;
+    f32x4* xs_mine = xs[par][hg][h][0];
+    const f32x4* xs_other = xs[par][hg][h ^ 1][0];
+    xs_mine[lane] = sp0;
+    xs_mine[kWave + lane] = sp1;
+    wait_vm_all();
+    __syncthreads();
+    if (n + 2 < ntiles) gather(D, (n + 2) * kRows);
+    const int tbase = n * kRows;
+    const f32x4 t0 = xs_other[lane];
+    const f32x4 t1 = xs_other[kWave + lane];
+    const f32x4 bias0 = *reinterpret_cast<const f32x4*>(bias + tbase + 4 * g);
+    const f32x4 bias1 = *reinterpret_cast<const f32x4*>(bias + tbase + 16 + 4 * g);
+    // both waves of the pair form the same sum in the same order
+    const f32x4 s0 = h ? (t0 + sp0) : (sp0 + t0);
+    const f32x4 s1 = h ? (t1 + sp1) : (sp1 + t1);
+    // ---- S^T of the next tile: the products run on the matrix cores while
+    // the softmax below runs on the vector ALUs.  Unconditional, so that both
+    // sit in one scheduling region: after the last tile it multiplies a stale
+    // buffer and the result is never used.
+    qk(Q, sp0, sp1);
+    // ---- operand A of O^T (value dims x rows), independent of P
+    v4i16 va[16], vb[16];
+    {
+      const unsigned char* vp = P + tr_base;
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb) {
+        va[mb] = tr_read(vp + 32 * mb);
+        vb[mb] = tr_read(vp + 32 * mb + 16 * kPitch);
       }
     }
-    xs_mine[lane] = s0;
-    xs_mine[kWave + lane] = s1;
-    lds_barrier();
-    {
-      const f32x4 t0 = xs_other[lane];
-      const f32x4 t1 = xs_other[kWave + lane];
-      // both waves of the pair form the same sum in the same order
-      s0 = h ? (t0 + s0) : (s0 + t0);
-      s1 = h ? (t1 + s1) : (s1 + t1);
-    }
-    f32x4 s[2] = {s0, s1};
     // ---- online softmax (log2 domain); lane holds rows 4g+r and 16+4g+r
+    float sv[8];
     float mt = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool valid = sm.rows[tbase + 16 * mb + 4 * g + r] >= 0;
-        s[mb][r] = valid ? s[mb][r] * scale_log2 : -INFINITY;
-        mt = fmaxf(mt, s[mb][r]);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = fmaf(s0[r], scale_log2, bias0[r]);
+      sv[4 + r] = fmaf(s1[r], scale_log2, bias1[r]);
+      mt = fmaxf(mt, fmaxf(sv[r], sv[4 + r]));
+    }
+    mt = max_over_rows(mt);
     // Lazy rescaling: the reference max m_run only moves when a tile's max
     // exceeds it by more than 2^kLazy.  P = 2^(s - m_run) then stays below
     // 2^kLazy, and O, l and the log-sum-exp all use the same reference, so the
@@ -278,57 +347,45 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
     const bool need = mt > m_run + kLazy;
     if (__any(need)) {
       const float m_new = need ? mt : m_run;
-      const float alpha = need ? exp2f(m_run - m_new) : 1.f;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[i] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
-    float p[2][4];
+    // m_run is -inf only while every row so far was masked; then every s is
+    // -inf and P is 0.
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
     float ls = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[mb][r] = (m_run == -INFINITY) ? 0.f : exp2f(s[mb][r] - m_run);
-        ls += p[mb][r];
-      }
+    for (int r = 0; r < 8; ++r) {
+      sv[r] = __builtin_amdgcn_exp2f(sv[r] - mref);
+      ls += sv[r];
+    }
     l_run += ls;
     i32x4 pb;
-    pb[0] = (int)pack_bf16x2(p[0][0], p[0][1]);
-    pb[1] = (int)pack_bf16x2(p[0][2], p[0][3]);
-    pb[2] = (int)pack_bf16x2(p[1][0], p[1][1]);
-    pb[3] = (int)pack_bf16x2(p[1][2], p[1][3]);
+    pb[0] = (int)cvt_pk_bf16(sv[0], sv[1]);
+    pb[1] = (int)cvt_pk_bf16(sv[2], sv[3]);
+    pb[2] = (int)cvt_pk_bf16(sv[4], sv[5]);
+    pb[3] = (int)cvt_pk_bf16(sv[6], sv[7]);
     const bf16x8 pbf = as_bf16x8(pb);
     // ---- O^T [256 x 16] += V^T . P^T for this wave's value dims
-    const unsigned char* vp = tile + tr_base;
-    static_assert(16 * kPitch == 18688, "tr_read8 offsets assume a 1168-byte pitch");
 #pragma unroll
-    for (int mb = 0; mb < 16; mb += 4) {
-      i32x2_t r[8];
-      tr_read8(vp + 32 * mb, r);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const i32x4 av = {r[2 * j][0], r[2 * j][1], r[2 * j + 1][0], r[2 * j + 1][1]};
-        o[mb + j] = mfma16_bf16(as_bf16x8(av), pbf, o[mb + j]);
-      }
+    for (int mb = 0; mb < 16; ++mb) {
+      const v4i16 pair[2] = {va[mb], vb[mb]};
+      o[mb] = mfma16_bf16(__builtin_bit_cast(bf16x8, pair), pbf, o[mb]);
     }
   };
 
-  // Tiles 0 and 1 are resident; afterwards the DMA of tile n+1 is issued just
-  // before tile n is multiplied and waited for after it.
-  for (int n = 0; n < ntiles; n += 2) {
-    if (n > 0 && n + 1 < ntiles)
-      gather_tile<NW>(sm.tile1, kvb, sm.rows + (n + 1) * kRows, lane, wave);
-    compute(sm.tile0, n * kRows);
-    wait_vm_all();
-    __syncthreads();
+  // Unrolled by three so that every buffer role is static.
+  for (int n = 0; n < ntiles; n += 3) {
+    step(n, tileA, tileB, tileC);
     if (n + 1 >= ntiles) break;
-    if (n + 2 < ntiles) gather_tile<NW>(sm.tile0, kvb, sm.rows + (n + 2) * kRows, lane, wave);
-    compute(sm.tile1, (n + 1) * kRows);
-    wait_vm_all();
-    __syncthreads();
+    step(n + 1, tileB, tileC, tileA);
+    if (n + 2 >= ntiles) break;
+    step(n + 2, tileC, tileA, tileB);
   }
+  __syncthreads();  // every wave is done with the tiles: they stage the output
 
   // ---- finish: total row sum over the four lane groups
   float l_tot = l_run;
@@ -338,15 +395,16 @@ __global__ __launch_bounds__(HGW * 2 * kWave) void sparse_mla_kernel(
   const float lse_v = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   // lane holds O^T[dim = 256 h + 16 mb + 4 g + r][head].  The wave's
   // [16 heads x 256 dims] bf16 block is staged in LDS (the tile buffers are
-  // free now; rows padded to 528 bytes) and written out as contiguous rows:
-  // a normalised partial (split-KV) or the final output.
-  static_assert(2 * HGW * 16 * kOutPitch <= 2 * kTileBytes, "output staging fits the tiles");
-  unsigned char* st = reinterpret_cast<unsigned char*>(&sm) + wave * (16 * kOutPitch);
+  // free now; rows padded to 528 bytes, half of the waves in each of two
+  // buffers) and written out as contiguous rows: a normalised partial
+  // (split-KV) or the final output.
+  static_assert(HGW * 16 * kOutPitch <= kTileBytes, "output staging fits the tiles");
+  unsigned char* st = (wave < HGW ? tileA : tileB) + (wave % HGW) * (16 * kOutPitch);
 #pragma unroll
   for (int mb = 0; mb < 16; ++mb) {
     uint2 pk;
-    pk.x = pack_bf16x2(o[mb][0] * inv, o[mb][1] * inv);
-    pk.y = pack_bf16x2(o[mb][2] * inv, o[mb][3] * inv);
+    pk.x = cvt_pk_bf16(o[mb][0] * inv, o[mb][1] * inv);
+    pk.y = cvt_pk_bf16(o[mb][2] * inv, o[mb][3] * inv);
     *reinterpret_cast<uint2*>(st + c16 * kOutPitch + 32 * mb + 8 * g) = pk;
   }
   __builtin_amdgcn_wave_barrier();
@@ -428,10 +486,12 @@ hipError_t launch_attn(const SplitPlan& p, const __bf16* q, const __bf16* kv, co
                        const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k, float sl2,
                        __bf16* out, float* lse, __bf16* part_o, float* part_lse,
                        hipStream_t stream) {
-  const dim3 grid(B * T * p.head_groups * p.n_split);
+  const int n_work = B * T * p.head_groups * p.n_split;
+  const int per_xcd = (n_work + 7) / 8;
+  const dim3 grid(DSA_ATTN_XCD ? 8 * per_xcd : n_work);
   hipLaunchKernelGGL((sparse_mla_kernel<HGW>), grid, dim3(HGW * 2 * kWave), 0, stream, q, kv,
                      idx, ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, out, lse, part_o,
-                     part_lse, p.n_split, p.head_groups);
+                     part_lse, p.n_split, p.head_groups, n_work, per_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
   hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, (Hq + kCombHeads - 1) / kCombHeads),
