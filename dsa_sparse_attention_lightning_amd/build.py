@@ -25,11 +25,9 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 
-# Per-source extra flags.  sparse_mla keeps its MFMA accumulators in ordinary
-# VGPRs: its online-softmax rescale touches the O accumulator with VALU
-# instructions, and AGPR-resident accumulators would be copied out and back
-# around that code on every tile.
-EXTRA = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none at present: the attention kernel keeps its
+# O accumulator in AGPRs, pinned there in the source).
+EXTRA = {}
 
 
 def hipcc() -> str:
