@@ -63,14 +63,19 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 // ---------------------------------------------------------------- scans
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4, 8 inside each 16-lane row, then lane
+// 15's total is added to rows 1 and 3 and lane 31's to rows 2 and 3.  A lane
+// whose source lies outside its row receives 0.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
-  return x;
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return (uint32_t)v;
 }
 
 // Block-wide exclusive prefix sum of one value per thread.  `scratch` holds

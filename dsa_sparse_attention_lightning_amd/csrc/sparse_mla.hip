@@ -21,9 +21,10 @@
 //   * the 32 selected rows are gathered straight from HBM into LDS with
 //     16-byte LDS-DMA loads (buffer_load_dwordx4 ... lds);
 //   * the tile is stored row-major with a pitch of 74 16-byte chunks
-//     (1184 B) and the chunk index of rows 8..15 and 24..31 XOR-ed with 1:
-//     over the 64 LDS banks the 16-row operand reads of S^T and the 8-row
-//     transposing reads of O^T then touch every bank once, and every LDS
+//     (1184 B) and the chunk index of row r XOR-ed with bit 2 ^ bit 3 of r:
+//     the operand reads of S^T (8 or 16 rows per bank cycle) and the
+//     transposing reads of O^T (4 or 8 rows of 32 bytes) then hit distinct
+//     banks whether the LDS serves 32 or 64 banks per cycle, and every LDS
 //     address is one of two per-lane bases plus an immediate;
 //   * S^T reads 16-byte row fragments (operand A), lane group g covering
 //     latent dims [144 g, 144 g + 144) in 18 steps;
@@ -67,15 +68,18 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 
+// Chunk swizzle of tile row r: chunk c is stored at position c ^ swz(r).
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
 // Slot of one 16-byte LDS-DMA load inside a tile: instruction i of the tile
 // writes slots 64 i .. 64 i + 63; slot p is chunk position p % 74 of row
-// p / 74, which holds logical chunk position ^ bit 3 of the row.  The two
-// pad positions of a row receive a harmless copy of the row's chunk 0.
-// Packed as (row << 16) | byte offset of the chunk in the source row.
+// p / 74, which holds chunk position ^ swz(row).  The two pad positions of a
+// row receive a harmless copy of the row's chunk 0.  Packed as
+// (row << 16) | byte offset of the chunk in the source row.
 __device__ __forceinline__ int gather_slot(int i, int lane) {
   const int p = i * kWave + lane;
   const int r = p / kPitchChunks;
-  int c = (p - r * kPitchChunks) ^ ((r >> 3) & 1);
+  int c = (p - r * kPitchChunks) ^ swz(r);
   if (c >= kChunks) c = 0;
   return (r << 16) | (c * 16);
 }
@@ -297,14 +301,14 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
 
   // Per-lane LDS byte offsets that do not depend on the tile.
   // S^T operand A: row 16 mb + c16, logical chunk 18 g + i at position
-  // (18 g + i) ^ x with x = bit 3 of the row: +16 x for even i, -16 x for odd.
-  const int xq = (c16 >> 3) & 1;
+  // (18 g + i) ^ x with x = swz(row): +16 x for even i, -16 x for odd.
+  const int xq = swz(c16);
   const int qk_even = c16 * kPitch + 288 * g + 16 * xq;
   const int qk_odd = c16 * kPitch + 288 * g - 16 * xq;
   // O^T operand A (transposing reads): source row 4g + (c16 >> 2) (+16),
   // dims 16 mb + 4 (c16 & 3): the two chunks of a 32-byte window swap places
-  // in rows with bit 3 set (lane groups 2 and 3).
-  const int tr_base = (4 * g + (c16 >> 2)) * kPitch + ((8 * (c16 & 3)) ^ (16 * ((g >> 1) & 1)));
+  // where swz(row) = 1, i.e. for lane groups 1 and 2.
+  const int tr_base = (4 * g + (c16 >> 2)) * kPitch + ((8 * (c16 & 3)) ^ (16 * swz(4 * g)));
 
   // S^T operand reads of fragment i of one tile (dims 144 g + 8 i), rows
   // c16 and 16 + c16.
@@ -508,10 +512,21 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
   __bf16* dst = (n_split == 1)
                     ? out + ((int64_t)row * Hq + head - c16) * kDv
                     : part_o + (((int64_t)row * n_split + split) * Hq + head - c16) * kDv;
+  // One head row (1 KB) per instruction.  Split partials are streamed past
+  // the L2 (the combine reads them once, from another XCD's point of view),
+  // so the kernel does not end with megabytes of dirty lines to write back.
+  if (n_split == 1) {
 #pragma unroll
-  for (int hr = 0; hr < 16; ++hr) {  // one head row (1 KB) per instruction
-    const i32x4 v = *reinterpret_cast<const i32x4*>(st + hr * kOutPitch + 16 * lane);
-    *reinterpret_cast<i32x4*>(dst + (int64_t)hr * kDv + 8 * lane) = v;
+    for (int hr = 0; hr < 16; ++hr) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(st + hr * kOutPitch + 16 * lane);
+      *reinterpret_cast<i32x4*>(dst + (int64_t)hr * kDv + 8 * lane) = v;
+    }
+  } else {
+#pragma unroll
+    for (int hr = 0; hr < 16; ++hr) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(st + hr * kOutPitch + 16 * lane);
+      __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(dst + (int64_t)hr * kDv + 8 * lane));
+    }
   }
   if (g == 0) {
     if (n_split == 1) {

@@ -388,6 +388,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     return;  // the chunk kernels touched nothing for this row
   }
   uint32_t* hg = hist_g + (int64_t)row * kBins1;
+  // the histogram and the slice counts are loaded together
+  const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
   for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = hg[i];
   __syncthreads();
   select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
@@ -401,9 +403,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     return;
   }
   // concatenate the chunk slices in chunk order: prefix sum of the slice
-  // counts, then every thread copies entries of the flattened list
+  // counts, then each slice is copied by its own group of tpc threads
   {
-    const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
     uint32_t tot;
     const uint32_t ex = block_excl_scan<kTkWaves>(cnt, sm.scan, tot);
     if (tid < n_chunks) sm.chunk_off[tid] = ex;
@@ -412,31 +413,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   __syncthreads();
   const uint32_t* ck = cand_key + (int64_t)row * Lmax;
   const int32_t* cp = cand_pos + (int64_t)row * Lmax;
-  // gather in batches of kGather entries per thread, all loads issued first
-  for (uint32_t e0 = 0; e0 < listed; e0 += kGather * kTkThreads) {
-    uint32_t kv[kGather];
-    int32_t pv[kGather];
+  const int tpc = kTkThreads / n_chunks;
+  const int c = tid / tpc;
+  if (c < n_chunks) {
+    const int sub = tid - c * tpc;
+    const uint32_t off = sm.chunk_off[c];
+    const int cn = (int)(sm.chunk_off[c + 1] - off);
+    const int64_t base = (int64_t)c * chunk;
+    // batches of kGather entries per thread, all loads issued first
+    for (int e0 = sub; e0 < cn; e0 += kGather * tpc) {
+      uint32_t kv[kGather];
+      int32_t pv[kGather];
 #pragma unroll
-    for (int u = 0; u < kGather; ++u) {
-      const uint32_t e = e0 + u * kTkThreads + tid;
-      int64_t at = 0;
-      if (e < listed) {
-        int lo = 0, hi = n_chunks - 1;  // last chunk with chunk_off <= e
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sm.chunk_off[mid] <= e) lo = mid; else hi = mid - 1;
-        }
-        at = (int64_t)lo * chunk + (e - sm.chunk_off[lo]);
+      for (int u = 0; u < kGather; ++u) {
+        const int e = min(e0 + u * tpc, cn - 1);
+        kv[u] = ck[base + e];
+        pv[u] = cp[base + e];
       }
-      kv[u] = ck[at];
-      pv[u] = cp[at];
-    }
 #pragma unroll
-    for (int u = 0; u < kGather; ++u) {
-      const uint32_t e = e0 + u * kTkThreads + tid;
-      if (e < listed) {
-        sm.list_key[e] = kv[u];
-        sm.list_pos[e] = pv[u];
+      for (int u = 0; u < kGather; ++u) {
+        const int e = e0 + u * tpc;
+        if (e < cn) {
+          sm.list_key[off + e] = kv[u];
+          sm.list_pos[off + e] = pv[u];
+        }
       }
     }
   }
