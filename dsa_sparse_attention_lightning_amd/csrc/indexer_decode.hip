@@ -12,8 +12,9 @@
 //   B = k^T [D x 32 keys]    (32-key column blocks of an 8 KB key tile)
 //   C       [32 heads x 32 keys] fp32
 //
-// Each wave streams a contiguous run of 8 KB key tiles (64 fp8 or 32 bf16
-// rows of D = 128) with fully coalesced 16-byte loads, three tiles in flight,
+// Each wave streams 8 KB key tiles (64 fp8 or 32 bf16 rows of D = 128), the
+// waves of a row interleaved tile by tile, with fully coalesced 16-byte
+// loads, three tiles in flight,
 // and regroups each tile through its own LDS region so that lane l holds
 // D*e/2 contiguous bytes of key (l & 31).  The epilogue applies ReLU and the
 // per-head weight w' = w (bf16) or w * q_scale (fp8: the positive per-row
@@ -27,6 +28,7 @@ namespace dsa {
 namespace {
 
 constexpr int kDecWaves = 4;
+
 constexpr int kTileBytes = 8192;   // key bytes per wave step
 
 template <int D, bool FP8, int HB>
@@ -54,9 +56,16 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   const int b = row / T;
   const int t = row - b * T;
   const int tiles = (Lmax + TK - 1) / TK;
-  const int tile0 = (blockIdx.x * kDecWaves + wave) * tiles_per_wave;
-  if (tile0 >= tiles) return;
-  const int tend = min(tile0 + tiles_per_wave, tiles);
+  // Wave w of the row's W waves takes tiles w, w + W, w + 2W, ...: all
+  // waves sweep the row together, front to back (measurably closer to plain
+  // streaming bandwidth than giving each wave its own contiguous run).  The
+  // loop below runs over the wave's sequence numbers j = 0, 1, ...
+  const int first = blockIdx.x * kDecWaves + wave;
+  const int wstride = gridDim.x * kDecWaves;
+  if (first >= tiles) return;
+  const int tile0 = 0;
+  const int tend = min(tiles_per_wave, (tiles - first + wstride - 1) / wstride);
+  auto tmap = [&](int j) { return first + j * wstride; };
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
@@ -92,7 +101,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   // multiplied (the loop is unrolled by three so every buffer is static).
   i32x4 ba[NL], bb[NL], bc[NL];
   float sa[CB], sb[CB], sc_[CB];
-  auto load = [&](int tile, i32x4(&buf)[NL], float(&bs)[CB]) {
+  auto load = [&](int seq, i32x4(&buf)[NL], float(&bs)[CB]) {
+    const int tile = tmap(seq);
 #pragma unroll
     for (int v = 0; v < NL; ++v) {
       const int off = 16 * lane + 1024 * v;  // byte offset in the tile
@@ -104,7 +114,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
       for (int c = 0; c < CB; ++c) bs[c] = ksb[min(tile * TK + c * 32 + col, Lmax - 1)];
     }
   };
-  auto compute = [&](int tile, const i32x4(&raw)[NL], const float(&cs)[CB]) {
+  auto compute = [&](int seq, const i32x4(&raw)[NL], const float(&cs)[CB]) {
+    const int tile = tmap(seq);
 #pragma unroll
     for (int v = 0; v < NL; ++v) {
       const int off = 16 * lane + 1024 * v;
@@ -182,9 +193,8 @@ hipError_t launch_dec(const void* q, const float* q_scale, const float* w, const
   const int rows = B * T;
   const int tk = kTileBytes / (D * (FP8 ? 1 : 2));
   const int tiles = (Lmax + tk - 1) / tk;
-  // Few long-lived waves (about 2 workgroups per CU): each takes a long
-  // contiguous run of key tiles, so its query fragments are loaded once and
-  // the DRAM stream of each wave stays sequential.
+  // Few long-lived waves (about 2 workgroups per CU), each taking many key
+  // tiles, so that its query fragments are loaded once.
   int64_t want_waves = (int64_t)DSA_DEC_WG_TARGET * kDecWaves;
   int tpw = (int)(((int64_t)rows * tiles + want_waves - 1) / want_waves);
   tpw = max(1, min(tpw, 64));
