@@ -138,18 +138,22 @@ size_t topk_region(const dsa_stack_shape_t* s) {
   return (b + 255) & ~size_t(255);
 }
 
+bool uses_prefill_indexer(int T, int H, int D) { return T > 1 && dsa::indexer_prefill_supported(H, D); }
+
+// row_hist: optional per-row top-k histogram filled on the way (decode kernel
+// only; pass null otherwise).
 dsa_status_t run_indexer(const void* q, dsa_dtype_t dtype, const float* q_scale, const float* w,
                          const void* k, const float* k_scale, const int32_t* ctx_len, int B,
                          int T, int H, int D, int Lmax, float* scores, int64_t ld,
-                         hipStream_t stream) {
+                         uint32_t* row_hist, hipStream_t stream) {
   const bool fp8 = dtype == DSA_FP8_E4M3;
   hipError_t e;
-  if (T > 1 && dsa::indexer_prefill_supported(H, D))
+  if (uses_prefill_indexer(T, H, D))
     e = dsa::launch_indexer_prefill(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax,
                                     scores, ld, stream);
   else
     e = dsa::launch_indexer_decode(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax,
-                                   scores, ld, stream);
+                                   scores, ld, row_hist, stream);
   return hip_status(e, "indexer launch");
 }
 
@@ -170,7 +174,7 @@ dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t dtype, const float* q
                                   Lmax, scores, ld_scores);
   if (st != DSA_OK) return st;
   return run_indexer(q, dtype, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax, scores,
-                     ld_scores, stream);
+                     ld_scores, nullptr, stream);
 }
 
 dsa_status_t dsa_topk_workspace_size(int B, int T, int Lmax, int k, size_t* bytes) {
@@ -192,7 +196,7 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx
         "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
   if (need) CHECK_PTR(workspace);
   return hip_status(dsa::launch_topk(scores, ld_scores, ctx_len, B, T, Lmax, k, idx, workspace,
-                                     workspace_bytes, stream),
+                                     workspace_bytes, false, stream),
                     "topk launch");
 }
 
@@ -285,16 +289,23 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
   const size_t tk_bytes = topk_region(shape);
   void* attn_ws = workspace ? static_cast<unsigned char*>(workspace) + tk_bytes : nullptr;
   dsa_stack_stats_t st_local = {0, 0, 0};
+  // When the decode indexer runs and the top-k keeps a per-row histogram, the
+  // indexer fills that histogram as it writes the scores and the top-k skips
+  // its own histogram pass.
+  uint32_t* row_hist = uses_prefill_indexer(s.T, s.H, s.D)
+                           ? nullptr
+                           : dsa::topk_row_hist(workspace, s.B, s.T, s.Lmax, s.k);
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer_t& L = layers[l];
     if (pattern[l] == 'F') {  // Full layer: fresh index set into the cache
       dsa_status_t st = run_indexer(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
                                     L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
-                                    score_buf, ld_scores, stream);
+                                    score_buf, ld_scores, row_hist, stream);
       if (st != DSA_OK) return st;
       st_local.n_indexer_calls++;
       st = hip_status(dsa::launch_topk(score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k,
-                                       idx_buf, workspace, tk_bytes, stream),
+                                       idx_buf, workspace, tk_bytes, row_hist != nullptr,
+                                       stream),
                       "topk launch");
       if (st != DSA_OK) return st;
       st_local.n_topk_calls++;

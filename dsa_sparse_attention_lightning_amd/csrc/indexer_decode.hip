@@ -30,13 +30,16 @@ namespace {
 constexpr int kDecWaves = 4;
 
 constexpr int kTileBytes = 8192;   // key bytes per wave step
+constexpr int kHistBits = 12;      // first radix digit of the top-k selection
+constexpr int kHistBins = 1 << kHistBits;
 
 template <int D, bool FP8, int HB>
 __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
-    int Lmax, float* __restrict__ scores, int64_t ld, int tiles_per_wave) {
+    int Lmax, float* __restrict__ scores, int64_t ld, int tiles_per_wave,
+    uint32_t* __restrict__ row_hist) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int ROWB = D * EB;            // bytes per key row
   constexpr int HALF = ROWB / 2;          // bytes of a row held by one lane
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   constexpr int PITCH = ROWB + 16;        // LDS row pitch (spreads banks)
   static_assert(NV >= 2 || !FP8, "fp8 needs 32 bytes per lane per MFMA step");
   __shared__ __align__(16) unsigned char stage[kDecWaves * TK * PITCH];
+  __shared__ uint32_t lhist[kHistBins];  // used when row_hist is given
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -62,9 +66,14 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   // loop below runs over the wave's sequence numbers j = 0, 1, ...
   const int first = blockIdx.x * kDecWaves + wave;
   const int wstride = gridDim.x * kDecWaves;
-  if (first >= tiles) return;
   const int tile0 = 0;
-  const int tend = min(tiles_per_wave, (tiles - first + wstride - 1) / wstride);
+  // (a wave past the row's last tile runs no iteration but stays for the
+  // workgroup barriers of the histogram)
+  const int tend = first < tiles ? min(tiles_per_wave, (tiles - first + wstride - 1) / wstride) : 0;
+  if (row_hist) {
+    for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
+    __syncthreads();
+  }
   auto tmap = [&](int j) { return first + j * wstride; };
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   unsigned char* my_stage = stage + wave * TK * PITCH;
@@ -162,13 +171,17 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
       const int key = tile * TK + c * 32 + col;
       if (g == 0 && key < Lmax) {
         float o = -INFINITY;
-        if (key <= pos) o = FP8 ? sc * cs[c] : sc;
+        if (key <= pos) {
+          o = FP8 ? sc * cs[c] : sc;
+          // top-k histogram: top 12 bits of the order-preserving key
+          if (row_hist) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);
+        }
         srow[key] = o;
       }
     }
     __builtin_amdgcn_wave_barrier();
   };
-  load(tile0, ba, sa);
+  if (tile0 < tend) load(tile0, ba, sa);
   if (tile0 + 1 < tend) load(tile0 + 1, bb, sb);
   for (int tile = tile0; tile < tend; tile += 3) {
     if (tile + 2 < tend) load(tile + 2, bc, sc_);
@@ -180,6 +193,14 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
     if (tile + 4 < tend) load(tile + 4, bb, sb);
     compute(tile + 2, bc, sc_);
   }
+  if (row_hist) {  // add this workgroup's counts to the row's histogram
+    __syncthreads();
+    uint32_t* rh = row_hist + (int64_t)row * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) {
+      const uint32_t c = lhist[i];
+      if (c) atomicAdd(&rh[i], c);
+    }
+  }
 }
 
 #ifndef DSA_DEC_WG_TARGET
@@ -189,7 +210,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
 template <int D, bool FP8, int HB>
 hipError_t launch_dec(const void* q, const float* q_scale, const float* w, const void* k,
                       const float* k_scale, const int32_t* ctx_len, int B, int T, int H,
-                      int Lmax, float* scores, int64_t ld, hipStream_t stream) {
+                      int Lmax, float* scores, int64_t ld, uint32_t* row_hist,
+                      hipStream_t stream) {
   const int rows = B * T;
   const int tk = kTileBytes / (D * (FP8 ? 1 : 2));
   const int tiles = (Lmax + tk - 1) / tk;
@@ -202,7 +224,7 @@ hipError_t launch_dec(const void* q, const float* q_scale, const float* w, const
   dim3 grid((tiles + per_block - 1) / per_block, rows);
   hipLaunchKernelGGL((indexer_decode_kernel<D, FP8, HB>), grid, dim3(kDecWaves * kWave), 0,
                      stream, (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, ctx_len,
-                     T, H, Lmax, scores, ld, tpw);
+                     T, H, Lmax, scores, ld, tpw, row_hist);
   return hipGetLastError();
 }
 
@@ -211,9 +233,10 @@ hipError_t launch_dec(const void* q, const float* q_scale, const float* w, const
 hipError_t launch_indexer_decode(const void* q, bool fp8, const float* q_scale, const float* w,
                                  const void* k, const float* k_scale, const int32_t* ctx_len,
                                  int B, int T, int H, int D, int Lmax, float* scores,
-                                 int64_t ld, hipStream_t stream) {
-#define DSA_DEC(DD, F8, HBB) \
-  return launch_dec<DD, F8, HBB>(q, q_scale, w, k, k_scale, ctx_len, B, T, H, Lmax, scores, ld, stream)
+                                 int64_t ld, uint32_t* row_hist, hipStream_t stream) {
+#define DSA_DEC(DD, F8, HBB)                                                                    \
+  return launch_dec<DD, F8, HBB>(q, q_scale, w, k, k_scale, ctx_len, B, T, H, Lmax, scores, ld, \
+                                 row_hist, stream)
   const bool two = H > 32;
   if (D == 128) {
     if (fp8) { if (two) DSA_DEC(128, true, 2); DSA_DEC(128, true, 1); }

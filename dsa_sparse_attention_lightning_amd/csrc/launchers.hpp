@@ -9,11 +9,14 @@
 namespace dsa {
 
 // Indexer scores, one query row at a time, keys streamed from HBM (T == 1
-// decode, and the row-wise fallback for prefill).
+// decode, and the row-wise fallback for prefill).  With row_hist non-null the
+// kernel also adds, per row, the count of visible scores in each of the 4096
+// bins of their top 12 order-preserving key bits (the first histogram of the
+// top-k selection) into row_hist[row * 4096 + bin], which must start at zero.
 hipError_t launch_indexer_decode(const void* q, bool fp8, const float* q_scale, const float* w,
                                  const void* k, const float* k_scale, const int32_t* ctx_len,
                                  int B, int T, int H, int D, int Lmax, float* scores,
-                                 int64_t ld, hipStream_t stream);
+                                 int64_t ld, uint32_t* row_hist, hipStream_t stream);
 
 // Indexer scores for a prefill chunk (T > 1): MFMA tiles over (query, key).
 hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale, const float* w,
@@ -23,9 +26,14 @@ hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale,
 bool indexer_prefill_supported(int H, int D);
 
 size_t topk_workspace_bytes(int B, int T, int Lmax, int k);
+// The per-row histogram inside a top-k workspace, or null when this shape
+// does not use one (rows selected by one workgroup each).
+uint32_t* topk_row_hist(void* workspace, int B, int T, int Lmax, int k);
+// hist_ready: the workspace's row histogram was already filled for these
+// scores (by launch_indexer_decode), so the histogram pass is skipped.
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, int B, int T,
                        int Lmax, int k, int32_t* idx, void* workspace, size_t ws_bytes,
-                       hipStream_t stream);
+                       bool hist_ready, hipStream_t stream);
 
 size_t sparse_attn_workspace_bytes(int B, int T, int Hq, int k, int d_v);
 hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,

@@ -383,11 +383,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   const int row = blockIdx.x;
   const int n = visible(ctx_len, row, T, Lmax);
   int32_t* out = idx + (int64_t)row * k;
+  uint32_t* hg = hist_g + (int64_t)row * kBins1;
   if (n <= k) {
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
-    return;  // the chunk kernels touched nothing for this row
+    // the chunk kernels touched nothing for this row, but a fused
+    // histogram from the indexer may have
+    for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
+    return;
   }
-  uint32_t* hg = hist_g + (int64_t)row * kBins1;
   // the histogram and the slice counts are loaded together
   const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
   for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = hg[i];
@@ -501,9 +504,15 @@ size_t topk_workspace_bytes(int B, int T, int Lmax, int) {
          align256(rows * Lmax * 4) + align256(rows * Lmax * 4);
 }
 
+uint32_t* topk_row_hist(void* workspace, int B, int T, int Lmax, int) {
+  const TopkPlan p = plan_topk(B, T, Lmax);
+  if (!p.chunked || workspace == nullptr) return nullptr;
+  return carve(workspace, B * T, Lmax, p.n_chunks).hist;
+}
+
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, int B, int T,
                        int Lmax, int k, int32_t* idx, void* workspace, size_t,
-                       hipStream_t stream) {
+                       bool hist_ready, hipStream_t stream) {
   const size_t smem = sizeof(TopkSmem);
   const TopkPlan p = plan_topk(B, T, Lmax);
   const int rows = B * T;
@@ -516,8 +525,9 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
   }
   const TopkWs w = carve(workspace, rows, Lmax, p.n_chunks);
   const dim3 grid(p.n_chunks, rows);
-  hipLaunchKernelGGL(topk_chunk_hist_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
-                     ctx_len, T, Lmax, k, p.chunk, w.hist);
+  if (!hist_ready)
+    hipLaunchKernelGGL(topk_chunk_hist_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
+                       ctx_len, T, Lmax, k, p.chunk, w.hist);
   hipLaunchKernelGGL(topk_chunk_collect_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
                      ctx_len, T, Lmax, k, p.chunk, w.hist, w.key, w.pos, w.cnt, p.n_chunks);
   hipError_t e = set_smem_attr((const void*)topk_finish_kernel, smem);
