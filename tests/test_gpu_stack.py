@@ -116,3 +116,42 @@ def test_bad_pattern_rejected_before_launch(bad):
     with pytest.raises(dsa.DSAError) as e:
         st.run()
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("idx_dtype", ["fp8", "bf16"])
+def test_stack_fused_histogram_ragged(idx_dtype):
+    """Long rows take the chunked top-k, whose first histogram the decode
+    indexer builds inside the stack.  Rows with n <= k (every visible position
+    kept) and consecutive F layers must leave that histogram clean: each F
+    layer's set equals the standalone kernels' (indexer, then top-k with its
+    own histogram pass), for every row, and a second run of the same stack
+    reproduces it."""
+    s = gen.Shape(90, "fused histogram", 3, "FFS", B=3, T=1, ctx=32768, H=16, D=128,
+                  idx_dtype=idx_dtype, k=2048, Hq=0)
+    say("stack with fused histogram,", idx_dtype)
+    qi = gen.make_indexer_query(s, DEV)
+    kb = gen.make_key_base(s, DEV)
+    layers = []
+    for l in range(s.n_layers):
+        ki = gen.make_indexer_keys(s, l, kb, DEV)
+        layers.append(dict(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w, k_idx=ki.k,
+                           k_idx_scale=ki.k_scale))
+    # ragged: one row with fewer visible positions than k, one just above k
+    ctx_t = torch.tensor([1000, 2049, 32768], dtype=torch.int32, device=DEV)
+    for run in range(2):
+        for p in ("FFS", "FSF"):
+            st = dsa.Stack(p, layers, ctx_t, B=s.B, T=1, H=s.H, D=s.D, Lmax=s.Lmax, k=s.k, Hq=0,
+                           idx_dtype=s.idx_dtype, scale=s.scale)
+            st.run()
+            torch.cuda.synchronize()
+            last_f = max(i for i, c in enumerate(p) if c == "F")
+            L = layers[last_f]
+            sc = dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx_t, L["q_idx_scale"],
+                                    L["k_idx_scale"])
+            want = dsa.topk(sc, ctx_t, s.k)
+            torch.cuda.synchronize()
+            got = st.idx_buf.cpu().numpy()
+            assert np.array_equal(got, want.cpu().numpy()), (run, p)
+            assert np.array_equal(got[0, 0, :1000], np.arange(1000)) and np.all(got[0, 0, 1000:] == -1)
+            parity.check_topk_exact(got, sc.cpu().numpy(), [1000, 2049, 32768], s.k)
+            say(f"  run {run} pattern {p}: ok")
