@@ -16,8 +16,9 @@ Also reported on the same line:
     roofline of the dominant kernel;
   * the prefill chunk (8192 queries on a 65536-token context, fp8, plus the
     same shape in bf16): indexer scores TFLOP/s and top-k time;
-  * the fp64 CPU oracle timed on a bounded sample on this host.
-
+  * the same prefill chunk through a 4-layer stack with sparse attention on
+    every layer (all-F against FSSS): chunked prefill under IndexCache;
+  * the fp64 CPU oracle timed on a bounded sample on this host;
   * the pattern sweep at context 196608 (16 layers, batch 4): all-F, FS,
     FSSS, FSSSSSSS, with the overlap between each S layer's reused index set
     and the set its own indexer would select.
@@ -304,6 +305,44 @@ def prefill_bench(dev, reps=5):
     return out
 
 
+def prefill_stack_bench(dev, n_layers=4, reps=3):
+    """The prefill chunk (8192 queries appended to a 65536-token context, fp8
+    indexer) through a short layer stack with sparse MLA attention (128 heads)
+    on every layer: chunked prefill under IndexCache, all-F against FSSS."""
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    base = gen.CONFIGS[2]
+    s = gen.Shape(2, "prefill stack", n_layers, "F" * n_layers, B=base.B, T=base.T,
+                  ctx=base.ctx, H=base.H, D=base.D, idx_dtype=base.idx_dtype, k=base.k, Hq=128)
+    layers = build_decode_workload(s, dev)
+    ctx = gen.ctx_lens(s, dev)
+    out = {"workload": f"prefill chunk: {n_layers} layers, {s.T} queries on a {s.ctx}-token "
+                       f"context, indexer {s.H}x{s.D} {s.idx_dtype}, top-{s.k}, "
+                       f"MLA {s.Hq} heads x {s.d_qk} bf16"}
+    af = 2.0 * s.Hq * s.k * (s.d_qk + s.d_v) * s.B * s.T
+    for name, p in (("all-F", "F" * n_layers), ("FSSS", gen.tile_pattern("FSSS", n_layers))):
+        st = dsa.Stack(p, layers, ctx, **shape_kw(s))
+        ms, stats = time_stack(st, reps, 1)
+        del st
+        st_i = dsa.Stack(p, layers, ctx, **shape_kw(s, attn=False))
+        ms_i, _ = time_stack(st_i, reps, 1)
+        del st_i
+        att = (ms - ms_i) / n_layers
+        out[name] = dict(pattern=p, ms_per_chunk=round(ms, 3),
+                         tokens_per_s=round(s.B * s.T / (ms * 1e-3), 1),
+                         n_indexer_calls=stats["n_indexer_calls"],
+                         indexer_topk_ms=round(ms_i, 3),
+                         attention_ms_per_layer=round(att, 3),
+                         attention_tflops=round(af / (att * 1e-3) / 1e12, 1))
+        log(f"prefill stack {name}: {ms:.2f} ms per chunk ({s.B * s.T / (ms * 1e-3):.0f} tok/s), "
+            f"indexer+top-k {ms_i:.2f} ms, attention {att:.2f} ms/layer")
+    out["speedup_fsss_vs_allf"] = round(out["all-F"]["ms_per_chunk"] / out["FSSS"]["ms_per_chunk"], 3)
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(s, layers, budget_s):
     """The fp64 oracle, as it stands, on sequence 0 of the same workload."""
     import numpy as np
@@ -393,6 +432,7 @@ def main():
     if not args.no_sweep:
         sweep = pattern_sweep(dev, max(5, args.steps // 3), 2)
     prefill = None if args.no_prefill else prefill_bench(dev)
+    prefill_stack = None if args.no_prefill else prefill_stack_bench(dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s, layers, args.cpu_seconds)
@@ -424,6 +464,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "prefill": prefill,
+        "prefill_stack": prefill_stack,
         "pattern_sweep": sweep,
     }
     print(json.dumps(line), flush=True)

@@ -155,3 +155,41 @@ def test_stack_fused_histogram_ragged(idx_dtype):
             assert np.array_equal(got[0, 0, :1000], np.arange(1000)) and np.all(got[0, 0, 1000:] == -1)
             parity.check_topk_exact(got, sc.cpu().numpy(), [1000, 2049, 32768], s.k)
             say(f"  run {run} pattern {p}: ok")
+
+
+@pytest.mark.parametrize("idx_dtype,D,k,Hq", [("bf16", 64, 128, 32), ("fp8", 128, 512, 16)],
+                         ids=["bf16-k128-unsplit", "fp8-k512-split"])
+def test_prefill_stack_against_oracle(idx_dtype, D, k, Hq):
+    """A chunked-prefill stack under IndexCache: T query rows per sequence
+    (causal, row t sees keys <= ctx - T + t), ragged contexts, the F/S branch,
+    the prefill indexer kernel and sparse attention over per-row index sets
+    (with and without split-KV), against the fp64 oracle's stack."""
+    s = gen.Shape(91, "prefill stack", 4, "FSFS", B=2, T=24, ctx=1536, H=8, D=D,
+                  idx_dtype=idx_dtype, k=k, Hq=Hq)
+    say("prefill stack", idx_dtype, "k", k, "Hq", Hq)
+    layers = build_layers(s)
+    ctx = [1536, 1000]
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    st = dsa.Stack(s.pattern, layers, ctx_t, **shape_kwargs(s))
+    stats = st.run()
+    torch.cuda.synchronize()
+    assert stats["n_indexer_calls"] == 2 and stats["n_attn_calls"] == 4
+    ol = oracle_layers(layers, s)
+    ref = oracle.run_stack(s.pattern, ol, ctx, s.k, s.scale, s.d_v)
+    used = None
+    for l, c in enumerate(s.pattern):
+        if c == "F":
+            L = layers[l]
+            sc = dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx_t, L["q_idx_scale"],
+                                    L["k_idx_scale"])
+            used = dsa.topk(sc, ctx_t, s.k).cpu().numpy()
+            osc = oracle.indexer_scores(ol[l]["q_idx"], ol[l]["w"], ol[l]["k_idx"], ctx)
+            parity.check_scores(sc.cpu().numpy()[..., :s.Lmax].astype(np.float64), osc, idx_dtype)
+            parity.check_topk_exact(used, sc.cpu().numpy(), ctx, s.k)
+            parity.check_topk_boundary(used, osc, ctx, s.k)
+        ro, rl = oracle.sparse_attn(ol[l]["q"], ol[l]["kv"], used, ctx, s.scale, s.d_v)
+        parity.check_attn(layers[l]["out"].float().cpu().numpy(), layers[l]["lse"].cpu().numpy(),
+                          ro, rl)
+        parity.check_attn(layers[l]["out"].float().cpu().numpy(), None, ref["out"][l], None)
+        say(f"  layer {l} {c}: ok")
+    assert np.array_equal(st.idx_buf.cpu().numpy(), used)
