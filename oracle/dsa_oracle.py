@@ -25,6 +25,17 @@ Attention via Cross-Layer Index Reuse", gist.science es/pt/it/de editions):
   first d_v columns.  Dense softmax over the valid selected rows.
 * dense_attn      - full causal attention, O(L^2): the baseline DSA replaces
   (technical summary §1); used only as a test pin.
+* kv_append       - the cache write that precedes the path in every step:
+  each new token's latent row and indexer key row are stored at its position
+  (pos = ctx_len[b] - T + t).  New rows arrive in fp32 and are encoded into
+  the cache's format: bfloat16 with round-to-nearest-even for the latent cache
+  and a bf16 key cache; for an fp8 key cache, one scale per row,
+  scale = amax / 448 (1 if the row is zero), and every value / scale rounded
+  to the nearest OCP E4M3FN code (ties to even).  The scale and the quotients
+  are fp32 operations, the precision the device uses, so that both sides take
+  the same code decisions.  The pages only say that the indices are computed
+  from the cached keys; the fp8 block format follows the fp8 workload
+  description the decode benchmark is quoted on.
 * run_stack       - the IndexCache layer loop: F layers run the indexer and
   top-k and store the index set; S layers skip both and reuse the set of the
   nearest preceding F layer (technical summary §2, "Arquitectura del Método" /
@@ -61,6 +72,10 @@ __all__ = [
     "run_stack",
     "validate_pattern",
     "overlap_fraction",
+    "bf16_encode",
+    "e4m3fn_encode",
+    "quantize_fp8_rows_f32",
+    "kv_append",
 ]
 
 
@@ -97,6 +112,83 @@ def e4m3fn_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     out = sign * mag
     out = np.where((e == 15) & (m == 7.0), np.nan, out)
     return out
+
+
+def bf16_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
+
+    The kept value is the float32 truncated to its upper 16 bits, plus one unit
+    in the last kept place when the dropped 16 bits exceed half a unit, or
+    equal it and the kept part is odd.  (NaN inputs are not expected.)"""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep = u >> np.uint64(16)
+    drop = u & np.uint64(0xFFFF)
+    up = (drop > 0x8000) | ((drop == 0x8000) & ((keep & np.uint64(1)) == 1))
+    return (keep + up.astype(np.uint64)).astype(np.uint16)
+
+
+def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
+    """float32 values with |x| < 464 -> OCP E4M3FN codes (uint8), round to
+    nearest, ties to even.
+
+    A magnitude a >= 2^-6 has a = f * 2^(e+1) with f in [0.5, 1) (frexp, exact):
+    its code keeps round((a / 2^e - 1) * 8) as the 3-bit mantissa m, and a
+    carry to m = 8 moves to the next exponent.  Below 2^-6 the codes are the
+    subnormals m * 2^-9, m = round(a * 2^9) (m = 8 is the smallest normal).
+    The sign of x (also of -0) is kept.  Magnitudes up to 464 round to 448,
+    the largest finite code (0x7E)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)   # exact widening
+    sign = np.signbit(x).astype(np.int64)
+    a = np.abs(x)
+    if np.any(a >= 464.0) or np.any(np.isnan(a)):
+        raise ValueError("e4m3fn_encode: value out of the finite range")
+    f, ex = np.frexp(a)
+    e = ex.astype(np.int64) - 1                     # a in [2^e, 2^(e+1))
+    m = np.rint((a / np.exp2(e.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    normal_code = ((e + 7) << 3) | m
+    sub_code = np.rint(a * 2.0 ** 9).astype(np.int64)  # 0..8
+    code = np.where(a >= 2.0 ** -6, normal_code, sub_code)
+    return ((sign << 7) | code).astype(np.uint8)
+
+
+def quantize_fp8_rows_f32(v: np.ndarray):
+    """Per-row fp8 quantisation in fp32 arithmetic: scale = amax / 448 (1 for
+    an all-zero row), codes = e4m3fn_encode(v / scale).  Returns (codes uint8,
+    scale float32)."""
+    v32 = np.asarray(v, dtype=np.float32)
+    amax = np.max(np.abs(v32), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (v32 / scale[..., None]).astype(np.float32)
+    return e4m3fn_encode(q), scale
+
+
+def kv_append(kv_cache: np.ndarray, k_cache: np.ndarray, k_scale, kv_new: np.ndarray,
+              k_new: np.ndarray, ctx_len: Sequence[int], fp8: bool):
+    """Write T new token rows per sequence into copies of the caches.
+
+    kv_cache [B,Lmax,d_qk] bf16 bits; k_cache [B,Lmax,D] (fp8 codes uint8 with
+    k_scale [B,Lmax] float32, or bf16 bits uint16 and k_scale None); kv_new
+    [B,T,d_qk] and k_new [B,T,D] float32.  Row t of sequence b goes to
+    position ctx_len[b] - T + t.  Returns (kv_cache, k_cache, k_scale)."""
+    kv_out = np.array(kv_cache, copy=True)
+    k_out = np.array(k_cache, copy=True)
+    s_out = None if k_scale is None else np.array(k_scale, copy=True)
+    B, T = kv_new.shape[0], kv_new.shape[1]
+    pos = query_positions(ctx_len, T)
+    for b in range(B):
+        for t in range(T):
+            p = int(pos[b, t])
+            kv_out[b, p] = bf16_encode(kv_new[b, t])
+            if fp8:
+                codes, sc = quantize_fp8_rows_f32(k_new[b, t][None])
+                k_out[b, p] = codes[0]
+                s_out[b, p] = sc[0]
+            else:
+                k_out[b, p] = bf16_encode(k_new[b, t])
+    return kv_out, k_out, s_out
 
 
 def dequant_fp8_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -312,6 +312,112 @@ def pin_stack_counts(o, cases):
         assert res["n_indexer_calls"] == c["expected_indexer_calls"]
 
 
+# ---------------------------------------------------------------- cache append
+
+def _finite_e4m3_values():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = ~np.isnan(vals)
+    return codes[fin], vals[fin]
+
+
+def pin_e4m3_encode_roundtrip(o):
+    # every finite code is reproduced from its own value (both zeros included)
+    codes, vals = _finite_e4m3_values()
+    got = o.e4m3fn_encode(vals.astype(np.float32))
+    assert np.array_equal(got, codes)
+
+
+def pin_e4m3_encode_bruteforce(o):
+    # nearest code by exhaustive search over the 254 finite codes; a tie goes
+    # to the code with the even mantissa (last bit 0)
+    codes, vals = _finite_e4m3_values()
+    r = RNG(11)
+    x = np.concatenate([r.uniform(-460, 460, 3000), r.normal(0, 1, 3000),
+                        r.normal(0, 2.0 ** -7, 2000),
+                        (vals[:, None] + vals[None, :]).ravel()[:: 7] / 2.0]).astype(np.float32)
+    x = x[np.abs(x.astype(np.float64)) < 464.0]
+    got = o.e4m3fn_encode(x)
+    xv = x.astype(np.float64)
+    for xi, gi in zip(xv, got):
+        d = np.abs(vals - xi)
+        best = np.flatnonzero(d == d.min())
+        best = best[np.signbit(vals[best]) == np.signbit(xi)] if len(best) > 1 else best
+        if len(best) > 1:
+            best = best[(codes[best] & 1) == 0]
+        assert codes[best[0]] == gi, (xi, hex(codes[best[0]]), hex(gi))
+
+
+def pin_e4m3_encode_library(o):
+    # torch's float32 -> float8_e4m3fn conversion rounds to nearest even
+    r = RNG(12)
+    x = np.concatenate([r.uniform(-448, 448, 20000), r.normal(0, 3, 20000)]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.e4m3fn_encode(x), ref)
+
+
+def pin_bf16_encode_library(o):
+    r = RNG(13)
+    x = np.concatenate([r.normal(0, 1, 50000), r.uniform(-1e4, 1e4, 50000)]).astype(np.float32)
+    # exact ties: a float32 whose dropped 16 bits are exactly 0x8000
+    base = r.normal(0, 100, 2000).astype(np.float32).view(np.uint32)
+    ties = (base & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.bf16_encode(x), ref)
+
+
+def pin_fp8_row_quantisation(o):
+    r = RNG(14)
+    v = r.normal(0, 2, (40, 128)).astype(np.float32)
+    v[3] = 0.0
+    codes, scale = o.quantize_fp8_rows_f32(v)
+    dec = o.e4m3fn_bits_to_f64(codes)
+    # the largest magnitude of each non-zero row maps to the largest code
+    amax_col = np.argmax(np.abs(v), axis=1)
+    nz = np.abs(v).max(axis=1) > 0
+    assert np.all(np.abs(dec[np.arange(40), amax_col])[nz] == 448.0)
+    assert scale[3] == 1.0 and np.all(codes[3] == 0)
+    # reconstruction within half a step of the format (relative 2^-4 for
+    # normals, absolute 2^-10 * scale for subnormals)
+    err = np.abs(dec * scale[:, None] - v.astype(np.float64))
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+def pin_kv_append(o):
+    r = RNG(15)
+    B, T, L, dqk, D = 3, 4, 20, 12, 8
+    ctx = [20, 9, 4]
+    kv = r.integers(0, 1 << 16, (B, L, dqk), dtype=np.uint32).astype(np.uint16)
+    k8 = r.integers(0, 256, (B, L, D), dtype=np.uint32).astype(np.uint8)
+    ks = r.uniform(0.1, 1, (B, L)).astype(np.float32)
+    kv_new = r.normal(0, 1, (B, T, dqk)).astype(np.float32)
+    k_new = r.normal(0, 1, (B, T, D)).astype(np.float32)
+    kv2, k2, s2 = o.kv_append(kv, k8, ks, kv_new, k_new, ctx, True)
+    for b in range(B):
+        written = set(range(ctx[b] - T, ctx[b]))
+        for p in range(L):
+            if p in written:
+                t = p - (ctx[b] - T)
+                assert np.array_equal(kv2[b, p], torch.from_numpy(kv_new[b, t]).to(
+                    torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+                ref = torch.from_numpy(k_new[b, t] / s2[b, p]).to(torch.float8_e4m3fn)
+                assert np.array_equal(k2[b, p], ref.view(torch.uint8).numpy())
+                assert s2[b, p] == np.float32(np.abs(k_new[b, t]).max() / np.float32(448.0))
+            else:   # nothing else moves
+                assert np.array_equal(kv2[b, p], kv[b, p]) and np.array_equal(k2[b, p], k8[b, p])
+                assert s2[b, p] == ks[b, p]
+    kb = r.integers(0, 1 << 16, (B, L, D), dtype=np.uint32).astype(np.uint16)
+    _, kb2, none = o.kv_append(kv, kb, None, kv_new, k_new, ctx, False)
+    assert none is None
+    for b in range(B):
+        p0 = ctx[b] - T
+        assert np.array_equal(kb2[b, p0:ctx[b]], torch.from_numpy(k_new[b]).to(
+            torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
 ALL_PINS = [
     pin_e4m3_table, pin_e4m3_values, pin_bf16_table,
     pin_indexer_closed_form, pin_indexer_bruteforce, pin_indexer_library,
@@ -320,4 +426,6 @@ ALL_PINS = [
     pin_attn_dense_equiv, pin_attn_single_row, pin_attn_zero_query,
     pin_attn_perm_and_padding, pin_attn_bruteforce,
     pin_stack_semantics, pin_stack_identical_keys,
+    pin_e4m3_encode_roundtrip, pin_e4m3_encode_bruteforce, pin_e4m3_encode_library,
+    pin_bf16_encode_library, pin_fp8_row_quantisation, pin_kv_append,
 ]

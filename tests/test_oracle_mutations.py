@@ -107,6 +107,61 @@ def _stack_reuse_first_f(o):
     return f
 
 
+def _bf16_truncate(o):
+    def f(x):
+        u = np.asarray(x, dtype=np.float32).view(np.uint32)
+        return (u >> np.uint32(16)).astype(np.uint16)
+    return f
+
+
+def _e4m3_encode(o, half_up=False, normal_from=2.0 ** -6):
+    def f(x):
+        x = np.asarray(x, dtype=np.float32).astype(np.float64)
+        if np.any(np.abs(x) >= 464.0):
+            raise ValueError("out of range")
+        rnd = (lambda v: np.floor(v + 0.5)) if half_up else np.rint
+        sign = np.signbit(x).astype(np.int64)
+        a = np.abs(x)
+        _, ex = np.frexp(a)
+        e = ex.astype(np.int64) - 1
+        m = rnd((a / np.exp2(e.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+        e = np.where(m == 8, e + 1, e)
+        m = np.where(m == 8, 0, m)
+        normal = ((e + 7) << 3) | m
+        sub = rnd(a * 2.0 ** 9).astype(np.int64)
+        code = np.where(a >= normal_from, normal, sub)
+        return ((sign << 7) | (code & 0x7F)).astype(np.uint8)
+    return f
+
+
+def _fp8_rows_scale(o, denom=447.0):
+    def f(v):
+        v32 = np.asarray(v, dtype=np.float32)
+        amax = np.max(np.abs(v32), axis=-1)
+        scale = np.where(amax > 0, amax / np.float32(denom), np.float32(1.0)).astype(np.float32)
+        q = np.clip(v32 / scale[..., None], -463.0, 463.0).astype(np.float32)
+        return o.e4m3fn_encode(q), scale
+    return f
+
+
+def _kv_append_shifted(o):
+    def f(kv_cache, k_cache, k_scale, kv_new, k_new, ctx_len, fp8):
+        kv_out, k_out = np.array(kv_cache, copy=True), np.array(k_cache, copy=True)
+        s_out = None if k_scale is None else np.array(k_scale, copy=True)
+        B, T = kv_new.shape[0], kv_new.shape[1]
+        for b in range(B):
+            for t in range(T):
+                p = min(int(ctx_len[b]) - T + t + 1, kv_cache.shape[1] - 1)
+                kv_out[b, p] = o.bf16_encode(kv_new[b, t])
+                if fp8:
+                    c, sc = o.quantize_fp8_rows_f32(k_new[b, t][None])
+                    k_out[b, p], s_out[b, p] = c[0], sc[0]
+                else:
+                    k_out[b, p] = o.bf16_encode(k_new[b, t])
+        return kv_out, k_out, s_out
+    return f
+
+
 MUTANTS = {
     "indexer_no_relu": ("indexer_scores_row", lambda o: _indexer_row(relu=False)),
     "indexer_w_inside_relu": ("indexer_scores_row", lambda o: _indexer_row(w_inside=True)),
@@ -122,6 +177,11 @@ MUTANTS = {
     "attn_values_wrong_slice": ("_softmax_attend", lambda o: _attend(value_slice_end=True)),
     "attn_padding_not_ignored": ("sparse_attn", _sparse_attn_no_filter),
     "stack_reuses_first_f": ("run_stack", _stack_reuse_first_f),
+    "bf16_encode_truncates": ("bf16_encode", _bf16_truncate),
+    "e4m3_encode_ties_away": ("e4m3fn_encode", lambda o: _e4m3_encode(o, half_up=True)),
+    "e4m3_encode_subnormal_edge": ("e4m3fn_encode", lambda o: _e4m3_encode(o, normal_from=2.0 ** -7)),
+    "fp8_rows_scale_447": ("quantize_fp8_rows_f32", _fp8_rows_scale),
+    "kv_append_row_off_by_one": ("kv_append", _kv_append_shifted),
 }
 
 
