@@ -18,6 +18,8 @@ Also reported on the same line:
     same shape in bf16): indexer scores TFLOP/s and top-k time;
   * the same prefill chunk through a 4-layer stack with sparse attention on
     every layer (all-F against FSSS): chunked prefill under IndexCache;
+  * the KV-cache append (latent bf16 + fp8 indexer key rows) at the decode
+    and prefill-chunk shapes, which precedes the path in every step;
   * the fp64 CPU oracle timed on a bounded sample on this host;
   * the pattern sweep at context 196608 (16 layers, batch 4): all-F, FS,
     FSSS, FSSSSSSS, with the overlap between each S layer's reused index set
@@ -343,6 +345,48 @@ def prefill_stack_bench(dev, n_layers=4, reps=3):
     return out
 
 
+def kv_append_bench(dev, reps=200):
+    """KV-cache append (latent row bf16 + fp8 indexer key with its row scale)
+    at the decode shape (batch 8, one token, 131072-row caches) and the prefill
+    chunk (8192 tokens into a 65536-row cache).  Algorithmic bytes per token
+    row: fp32 reads of d_qk + D values, bf16 latent write, fp8 key write and
+    one fp32 scale."""
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    d_qk, D = 576, 128
+    row_bytes = 4 * (d_qk + D) + 2 * d_qk + D + 4
+    out = {"bytes_per_row": row_bytes}
+    for name, B, T, Lmax in (("decode", 8, 1, 131072), ("prefill", 1, 8192, 65536)):
+        kvc = torch.zeros((B, Lmax, d_qk), dtype=torch.bfloat16, device=dev)
+        kc = torch.zeros((B, Lmax, D), dtype=torch.float8_e4m3fn, device=dev)
+        ks = torch.ones((B, Lmax), dtype=torch.float32, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234)
+        kvn = torch.randn((B, T, d_qk), generator=g, device=dev)
+        kn = torch.randn((B, T, D), generator=g, device=dev)
+        ctx = torch.full((B,), Lmax, dtype=torch.int32, device=dev)
+        # The decode append is far shorter than one host-side call, so the
+        # appends are captured into a HIP graph (20 per replay) and the graph
+        # is timed: the figure is device time, not the binding's call rate.
+        per = 20
+        for _ in range(3):
+            dsa.kv_append(ctx, kvn, kvc, kn, kc, ks)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per):
+                dsa.kv_append(ctx, kvn, kvc, kn, kc, ks)
+        ms = event_time_ms(lambda i=0: graph.replay(), max(1, reps // per), 1) / per
+        del graph
+        gbs = B * T * row_bytes / (ms * 1e-3) / 1e9
+        out[name] = dict(batch=B, tokens=T, cache_rows=Lmax, us=round(ms * 1e3, 2),
+                         gbs=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        log(f"kv append {name}: {ms * 1e3:.2f} us ({gbs:.0f} GB/s)")
+        del kvc, kc, ks, kvn, kn
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(s, layers, budget_s):
     """The fp64 oracle, as it stands, on sequence 0 of the same workload."""
     import numpy as np
@@ -401,6 +445,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 196K-context pattern sweep")
+    ap.add_argument("--kv-append-only", action="store_true",
+                    help="run only the KV-cache append leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference for hardware traffic counters)")
@@ -426,6 +472,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.kv_append_only:
+        print(json.dumps({"kv_append": kv_append_bench(dev)}), flush=True)
+        return
     s, layers, res, cut, kernels, roof = decode_bench(args, dev)
     main_res = res["config"]
     sweep = None
@@ -433,6 +482,7 @@ def main():
         sweep = pattern_sweep(dev, max(5, args.steps // 3), 2)
     prefill = None if args.no_prefill else prefill_bench(dev)
     prefill_stack = None if args.no_prefill else prefill_stack_bench(dev)
+    kv_app = kv_append_bench(dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s, layers, args.cpu_seconds)
@@ -465,6 +515,7 @@ def main():
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "prefill": prefill,
         "prefill_stack": prefill_stack,
+        "kv_append": kv_app,
         "pattern_sweep": sweep,
     }
     print(json.dumps(line), flush=True)

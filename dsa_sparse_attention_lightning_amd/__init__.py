@@ -7,6 +7,7 @@ must be contiguous device tensors; work is enqueued on torch's current stream.
     indexer_scores(q, w, k, ctx_len, q_scale=None, k_scale=None) -> scores [B,T,Lmax]
     topk(scores, ctx_len, k)                                     -> idx [B,T,k] int32
     sparse_attn(q, kv, idx, ctx_len, scale)                      -> (out, lse)
+    kv_append(ctx_len, kv_new, kv_cache, k_new, k_cache, k_scale) -> None (caches in place)
     run_stack(pattern, layers, ...)                              -> stats dict
 """
 from __future__ import annotations
@@ -18,7 +19,7 @@ from . import _lib
 from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
 
 __all__ = ["indexer_scores", "topk", "topk_workspace_size", "sparse_attn",
-           "sparse_attn_workspace_size", "run_stack",
+           "sparse_attn_workspace_size", "kv_append", "run_stack",
            "Stack", "DSAError", "library", "ld_for"]
 
 
@@ -155,6 +156,49 @@ def sparse_attn(q, kv, idx, ctx_len, scale: float, out=None, lse=None, want_lse=
                                    k, d_qk, d_v, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                                    need.value, _stream(stream)))
     return out, lse
+
+
+def kv_append(ctx_len, kv_new=None, kv_cache=None, k_new=None, k_cache=None, k_scale=None,
+              stream=None) -> None:
+    """Write T new token rows per sequence into the caches, in place.
+
+    kv_new [B,T,d_qk] fp32 -> kv_cache [B,Lmax,d_qk] bf16; k_new [B,T,D] fp32 ->
+    k_cache [B,Lmax,D] bf16, or float8_e4m3fn with k_scale [B,Lmax] fp32.  Row t
+    of sequence b lands at position ctx_len[b] - T + t.  Either pair may be
+    omitted."""
+    torch = _torch()
+    _need(ctx_len, "ctx_len", (torch.int32,), 1)
+    B = T = Lmax = None
+    d_qk = D = 0
+    dt = _lib.DSA_BF16
+    if kv_new is not None or kv_cache is not None:
+        _need(kv_new, "kv_new", (torch.float32,), 3)
+        _need(kv_cache, "kv_cache", (torch.bfloat16,), 3)
+        B, T, d_qk = kv_new.shape
+        Lmax = kv_cache.shape[1]
+        if kv_cache.shape[0] != B or kv_cache.shape[2] != d_qk:
+            raise TypeError("kv_cache must be [B, Lmax, d_qk] matching kv_new")
+    if k_new is not None or k_cache is not None:
+        _need(k_new, "k_new", (torch.float32,), 3)
+        _need(k_cache, "k_cache", (torch.bfloat16, torch.float8_e4m3fn), 3)
+        Bk, Tk, D = k_new.shape
+        if B is not None and (Bk, Tk, k_cache.shape[1]) != (B, T, Lmax):
+            raise TypeError("k_new / k_cache disagree with kv_new / kv_cache on B, T or Lmax")
+        B, T, Lmax = Bk, Tk, k_cache.shape[1]
+        if k_cache.shape[0] != B or k_cache.shape[2] != D:
+            raise TypeError("k_cache must be [B, Lmax, D] matching k_new")
+        dt = _idx_dtype(k_cache)
+        if dt == _lib.DSA_FP8_E4M3:
+            _need(k_scale, "k_scale", (torch.float32,), 2)
+            if tuple(k_scale.shape) != (B, Lmax):
+                raise TypeError("k_scale must be [B, Lmax]")
+    if B is None:
+        raise TypeError("kv_append needs kv_new/kv_cache, k_new/k_cache or both")
+    if ctx_len.shape[0] != B:
+        raise TypeError("ctx_len must have B entries")
+    _lib.check(library().dsa_kv_append(_ptr(kv_new), _ptr(k_new), _ptr(ctx_len), B, T, Lmax,
+                                       d_qk, D, dt, _ptr(kv_cache), _ptr(k_cache), _ptr(k_scale),
+                                       _stream(stream)))
 
 
 class Stack:

@@ -44,6 +44,8 @@ SIGNATURES = {
     "dsa_sparse_attn_workspace_size": (c_int, [c_int, c_int, c_int, c_int, c_int, c_size_p]),
     "dsa_sparse_attn": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                 c_int, c_f32, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "dsa_kv_append": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_vp,
+                              c_vp, c_vp, c_vp]),
     "indexcache_stack_workspace_size": (c_int, [ctypes.POINTER(StackShape), c_size_p]),
     "indexcache_run_stack": (c_int, [ctypes.c_char_p, c_int, ctypes.POINTER(Layer),
                                      ctypes.POINTER(StackShape), c_vp, c_vp, c_vp, c_i64, c_vp,

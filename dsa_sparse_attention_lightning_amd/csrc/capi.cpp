@@ -227,6 +227,53 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                     "sparse attention launch");
 }
 
+dsa_status_t dsa_kv_append(const float* kv_new, const float* k_new, const int32_t* ctx_len,
+                           int B, int T, int Lmax, int d_qk, int D, dsa_dtype_t k_dtype,
+                           void* kv_cache, void* k_cache, float* k_scale, hipStream_t stream) {
+  const char* fn = "dsa_kv_append";
+  CHECK(B >= 1 && T >= 1 && Lmax >= 1, DSA_ERR_INVALID_ARG,
+        "%s: need B, T, Lmax >= 1 (got %d, %d, %d)", fn, B, T, Lmax);
+  CHECK(T <= Lmax, DSA_ERR_INVALID_ARG, "%s: T (%d) exceeds Lmax (%d)", fn, T, Lmax);
+  CHECK((kv_new == nullptr) == (kv_cache == nullptr), DSA_ERR_INVALID_ARG,
+        "%s: kv_new and kv_cache must be given together", fn);
+  CHECK((k_new == nullptr) == (k_cache == nullptr), DSA_ERR_INVALID_ARG,
+        "%s: k_new and k_cache must be given together", fn);
+  CHECK(kv_new != nullptr || k_new != nullptr, DSA_ERR_INVALID_ARG,
+        "%s: nothing to append (both row pointers are NULL)", fn);
+  CHECK_PTR(ctx_len);
+  bool fp8 = false;
+  if (kv_new != nullptr) {
+    CHECK(d_qk >= 4 && d_qk <= 4096 && d_qk % 4 == 0, DSA_ERR_UNSUPPORTED,
+          "%s: d_qk must be a multiple of 4 in 4..4096 (got %d)", fn, d_qk);
+    CHECK_PTR(kv_new);
+    CHECK_PTR(kv_cache);
+  } else {
+    d_qk = 0;
+  }
+  if (k_new != nullptr) {
+    CHECK(k_dtype == DSA_BF16 || k_dtype == DSA_FP8_E4M3, DSA_ERR_INVALID_ARG,
+          "%s: unknown dtype %d", fn, (int)k_dtype);
+    CHECK(D >= 4 && D <= 256 && D % 4 == 0, DSA_ERR_UNSUPPORTED,
+          "%s: D must be a multiple of 4 in 4..256 (got %d)", fn, D);
+    CHECK_PTR(k_new);
+    CHECK_PTR(k_cache);
+    fp8 = k_dtype == DSA_FP8_E4M3;
+    if (fp8) {
+      CHECK(k_scale != nullptr, DSA_ERR_INVALID_ARG, "%s: an fp8 key cache needs k_scale", fn);
+      CHECK_PTR(k_scale);
+    } else {
+      CHECK(k_scale == nullptr, DSA_ERR_INVALID_ARG, "%s: a bf16 key cache takes no k_scale",
+            fn);
+    }
+  } else {
+    CHECK(k_scale == nullptr, DSA_ERR_INVALID_ARG, "%s: k_scale given without k_new", fn);
+    D = 0;
+  }
+  return hip_status(dsa::launch_kv_append(kv_new, k_new, ctx_len, B, T, Lmax, d_qk, D, fp8,
+                                          kv_cache, k_cache, k_scale, stream),
+                    "kv append launch");
+}
+
 dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* s, size_t* bytes) {
   const char* fn = "indexcache_stack_workspace_size";
   CHECK(s != nullptr && bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: NULL argument", fn);

@@ -41,4 +41,10 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                               float scale, void* out, float* lse, void* workspace,
                               size_t ws_bytes, hipStream_t stream);
 
+// New token rows into the latent cache (bf16) and the indexer key cache (bf16,
+// or fp8 with one fp32 scale per row).  A null kv_new / k_new skips that cache.
+hipError_t launch_kv_append(const float* kv_new, const float* k_new, const int32_t* ctx_len,
+                            int B, int T, int Lmax, int d_qk, int D, bool k_fp8, void* kv_cache,
+                            void* k_cache, float* k_scale, hipStream_t stream);
+
 }  // namespace dsa

@@ -131,6 +131,41 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                              int d_qk, int d_v, float scale, void* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * KV-cache append: the step that precedes the indexer and the attention in
+ * every decode step and prefill chunk.  During autoregressive generation each
+ * new token's key/value entries are added to the cache before it is attended
+ * over (enigmasecurity.cl article on IndexCache, section "Fundamentos de la
+ * Atención Dispersa en Transformadores"); under DSA a token brings two rows,
+ * its latent MLA row and its lightning-indexer key (technical summary §1).
+ *
+ *   row t of sequence b goes to position p = ctx_len[b] - T + t, i.e. ctx_len
+ *   already counts the T new tokens (the convention of every entry point).
+ *   kv_cache[b,p,:] = bf16_rne(kv_new[b,t,:])
+ *   k_cache[b,p,:]  = bf16_rne(k_new[b,t,:])                    (DSA_BF16)
+ *   k_scale[b,p]    = amax / 448 (1 for an all-zero row), fp32   (DSA_FP8_E4M3)
+ *   k_cache[b,p,:]  = e4m3fn_rne(k_new[b,t,:] / k_scale[b,p])   (fp32 division)
+ * The fp8 form is the one dsa_indexer_scores reads: one scale per key row (a
+ * 128-element block when D = 128).  Rounding is to nearest, ties to even;
+ * a quotient of magnitude >= 464 (reachable only through non-finite or
+ * out-of-range inputs) saturates to 448 instead of becoming NaN.
+ *
+ * kv_new   [B,T,d_qk] fp32, kv_cache [B,Lmax,d_qk] bf16 (in/out);
+ * k_new    [B,T,D] fp32,    k_cache  [B,Lmax,D] `k_dtype` (in/out),
+ * k_scale  [B,Lmax] fp32 (in/out) for DSA_FP8_E4M3, NULL for DSA_BF16.
+ * ctx_len  [B] int32 (device).
+ * Either pair may be skipped: kv_new and kv_cache both NULL (d_qk ignored)
+ * appends indexer keys only; k_new, k_cache and k_scale all NULL (D and
+ * k_dtype ignored) appends latent rows only; at least one pair is given.
+ * Only the T rows of each sequence are written; a row whose p falls outside
+ * 0..Lmax-1 is not written at all.  The new rows must not overlap the caches.
+ * Supported: d_qk and D multiples of 4, 4 <= d_qk <= 4096, 4 <= D <= 256,
+ * inputs finite.
+ */
+dsa_status_t dsa_kv_append(const float* kv_new, const float* k_new, const int32_t* ctx_len,
+                           int B, int T, int Lmax, int d_qk, int D, dsa_dtype_t k_dtype,
+                           void* kv_cache, void* k_cache, float* k_scale, hipStream_t stream);
+
 /* One layer's device tensors for indexcache_run_stack.  q_idx / w / k_idx
  * (and the fp8 scales) are read on F layers only; q / kv / out (and lse)
  * only when shape->Hq > 0. */

@@ -119,3 +119,23 @@ def test_stack_rejects_small_workspace(lib):
     st = lib.indexcache_run_stack(p, n, layers, ctypes.byref(shape), 16, 16, 16, 4096, 16,
                                   need.value - 1, None, None)
     assert st == _lib.DSA_ERR_WORKSPACE
+
+
+def test_kv_append_rejects_bad_arguments(lib):
+    f = lib.dsa_kv_append
+    # (kv_new, k_new, ctx, B, T, Lmax, d_qk, D, dtype, kv_cache, k_cache, k_scale, stream)
+    assert f(None, None, 16, 1, 1, 64, 576, 128, 1, None, None, None, None) == 1
+    assert "nothing to append" in _err(lib)
+    assert f(16, None, 16, 1, 1, 64, 576, 128, 1, None, None, None, None) == 1   # no kv_cache
+    assert "together" in _err(lib)
+    assert f(None, 16, 16, 1, 1, 64, 576, 128, 1, None, 16, None, None) == 1     # fp8, no scale
+    assert "k_scale" in _err(lib)
+    assert f(None, 16, 16, 1, 1, 64, 576, 128, 0, None, 16, 16, None) == 1       # bf16 + scale
+    assert f(16, None, 16, 1, 1, 64, 576, 128, 0, 16, None, 16, None) == 1       # scale, no keys
+    assert f(16, None, 16, 1, 1, 64, 574, 128, 0, 16, None, None, None) == 2     # d_qk % 4
+    assert f(None, 16, 16, 1, 1, 64, 576, 512, 1, None, 16, 16, None) == 2       # D > 256
+    assert f(None, 16, 16, 1, 1, 64, 576, 128, 5, None, 16, 16, None) == 1       # dtype
+    assert f(16, 16, 16, 1, 100, 64, 576, 128, 1, 16, 16, 16, None) == 1        # T > Lmax
+    assert f(16, 16, None, 1, 1, 64, 576, 128, 1, 16, 16, 16, None) == 1        # no ctx_len
+    assert f(16, 16, 16, 1, 1, 64, 576, 128, 1, 16, 18, 16, None) == 1          # misaligned
+    assert "aligned" in _err(lib)
