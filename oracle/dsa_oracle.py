@@ -36,6 +36,20 @@ Attention via Cross-Layer Index Reuse", gist.science es/pt/it/de editions):
   the same code decisions.  The pages only say that the indices are computed
   from the cached keys; the fp8 block format follows the fp8 workload
   description the decode benchmark is quoted on.
+* reuse_costs, pattern_cost, greedy_pattern_search - the training-free
+  pattern search (technical summary §2, part A of "Dos Enfoques de
+  Configuración" on the es edition, "Duas Abordagens de Otimização" on pt and
+  "Due Approcci di Configurazione" on it, "A. Training-Free IndexCache" under
+  "Methodik" on de): start from all layers F and convert one
+  layer at a time to S, each time the layer whose conversion raises the loss
+  least.  The pages measure the loss as LM loss on a calibration set; without
+  a trained model a PROXY stands in for it: the cost of a pattern is the sum,
+  over layers, of what layer l loses by attending with the index set of its
+  source layer (the nearest preceding F layer) instead of its own, either the
+  relative squared error of its attention output ("output") or the fraction
+  of its own selected positions missing from the reused set ("miss").  The
+  layers of the synthetic stack take independent inputs, so this sum is the
+  whole-stack difference against all-F, layer by layer.
 * run_stack       - the IndexCache layer loop: F layers run the indexer and
   top-k and store the index set; S layers skip both and reuse the set of the
   nearest preceding F layer (technical summary §2, "Arquitectura del Método" /
@@ -72,6 +86,10 @@ __all__ = [
     "run_stack",
     "validate_pattern",
     "overlap_fraction",
+    "reuse_costs",
+    "pattern_sources",
+    "pattern_cost",
+    "greedy_pattern_search",
     "bf16_encode",
     "e4m3fn_encode",
     "quantize_fp8_rows_f32",
@@ -407,3 +425,98 @@ def overlap_fraction(a: np.ndarray, b: np.ndarray) -> float:
     if not sa:
         return math.nan
     return len(sa & sb) / len(sa)
+
+
+# --------------------------------------------------------------------------
+# Training-free pattern search (greedy F -> S conversion, proxy loss)
+# --------------------------------------------------------------------------
+
+PROXIES = ("output", "miss")
+
+
+def reuse_costs(layers: List[Dict[str, np.ndarray]], ctx_len: Sequence[int], k: int,
+                scale: float, d_v: int, proxy: str = "output", idx_sets=None) -> np.ndarray:
+    """Cost matrix C [n, n]: C[l, j] for j < l is the proxy cost at layer l of
+    attending with layer j's index set instead of its own; C[l, l] = 0 and the
+    entries above the diagonal are 0 (never used: a source precedes its
+    layer).
+
+    own set T_l = topk(indexer_scores(layer l)) unless idx_sets[l] is given.
+    "output": sum over (b, t, head, value) of (o_l[T_j] - o_l[T_l])^2 divided
+              by the sum of o_l[T_l]^2 (0 / 0 = 0, x / 0 = inf), o_l[T] being
+              layer l's sparse attention output over set T;
+    "miss":   1 - (sum over rows of |T_j ∩ T_l|) / (sum over rows of |T_l|)
+              (0 when no row selects anything)."""
+    if proxy not in PROXIES:
+        raise ValueError(f"proxy must be one of {PROXIES}")
+    n = len(layers)
+    sets = list(idx_sets) if idx_sets is not None else [
+        topk(indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx_len), ctx_len, k)
+        for L in layers]
+    C = np.zeros((n, n))
+    if proxy == "output":
+        own = [sparse_attn(layers[l]["q"], layers[l]["kv"], sets[l], ctx_len, scale, d_v)[0]
+               for l in range(n)]
+        for l in range(n):
+            ref = float(np.sum(own[l] ** 2))
+            for j in range(l):
+                o = sparse_attn(layers[l]["q"], layers[l]["kv"], sets[j], ctx_len, scale, d_v)[0]
+                err = float(np.sum((o - own[l]) ** 2))
+                C[l, j] = err / ref if ref > 0 else (0.0 if err == 0 else math.inf)
+    else:
+        for l in range(n):
+            mine = sets[l].reshape(-1, sets[l].shape[-1])
+            for j in range(l):
+                theirs = sets[j].reshape(-1, sets[j].shape[-1])
+                common = total = 0
+                for r in range(mine.shape[0]):
+                    a = set(int(x) for x in mine[r] if x >= 0)
+                    common += len(a & set(int(x) for x in theirs[r] if x >= 0))
+                    total += len(a)
+                C[l, j] = 1.0 - common / total if total > 0 else 0.0
+    return C
+
+
+def pattern_sources(pattern: str) -> List[int]:
+    """src[l] = l for an F layer, the nearest preceding F layer for an S layer."""
+    validate_pattern(pattern, len(pattern))
+    src, last = [], 0
+    for l, c in enumerate(pattern):
+        if c == "F":
+            last = l
+        src.append(last)
+    return src
+
+
+def pattern_cost(pattern: str, C: np.ndarray) -> float:
+    """Proxy loss of a pattern: sum over layers, in layer order, of
+    C[l, src(l)] (F layers add C[l, l] = 0)."""
+    total = 0.0
+    for l, j in enumerate(pattern_sources(pattern)):
+        total += float(C[l, j])
+    return total
+
+
+def greedy_pattern_search(C: np.ndarray, n_shared: int):
+    """Greedy F -> S conversion.  Starting from all-F, each step tries every
+    F layer except layer 0 (an S layer needs a preceding F) as S and keeps the
+    conversion with the lowest pattern_cost; equal costs go to the lower
+    layer.  Returns [(pattern, cost)] after each of the n_shared steps."""
+    n = C.shape[0]
+    if not 0 <= n_shared <= n - 1:
+        raise ValueError(f"n_shared must be in 0..{n - 1}")
+    pattern = ["F"] * n
+    trace = []
+    for _ in range(n_shared):
+        best, best_cost = None, None
+        for l in range(1, n):
+            if pattern[l] != "F":
+                continue
+            cand = pattern.copy()
+            cand[l] = "S"
+            c = pattern_cost("".join(cand), C)
+            if best_cost is None or c < best_cost:
+                best, best_cost = cand, c
+        pattern = best
+        trace.append(("".join(pattern), best_cost))
+    return trace

@@ -418,6 +418,121 @@ def pin_kv_append(o):
             torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
 
 
+# ---------------------------------------------------------------- pattern search
+
+def _direct_pattern_cost(o, pattern, layers, ctx, k, scale, d_v, proxy):
+    """A pattern's proxy loss measured the long way: run the stack with the
+    pattern and with all-F and compare layer by layer."""
+    n = len(pattern)
+    run = o.run_stack(pattern, layers, ctx, k, scale, d_v)
+    ref = o.run_stack("F" * n, layers, ctx, k, scale, d_v)
+    total = 0.0
+    for l in range(n):
+        if proxy == "output":
+            d = math.fsum(((run["out"][l] - ref["out"][l]) ** 2).ravel())
+            z = math.fsum((ref["out"][l] ** 2).ravel())
+            total += d / z
+        else:
+            a = run["idx"][l].reshape(-1, k)
+            b = ref["idx"][l].reshape(-1, k)
+            hit = sum(np.intersect1d(a[i][a[i] >= 0], b[i][b[i] >= 0]).size
+                      for i in range(a.shape[0]))
+            total += 1.0 - hit / int((b >= 0).sum())
+    return total
+
+
+def pin_search_cost_decomposition(o):
+    """reuse_costs + pattern_cost equal the whole-stack difference against
+    all-F for every pattern of a 5-layer stack, for both proxies."""
+    r = RNG(21)
+    layers = _stack_layers(r, 5, B=2, T=2, L=24, H=3, D=6, Hq=2, dqk=10)
+    ctx, k, scale, dv = [24, 17], 5, 0.5, 6
+    for proxy in ("output", "miss"):
+        C = o.reuse_costs(layers, ctx, k, scale, dv, proxy)
+        assert np.all(C[np.triu_indices(5)] == 0)
+        for bits in itertools.product("FS", repeat=4):
+            p = "F" + "".join(bits)
+            want = _direct_pattern_cost(o, p, layers, ctx, k, scale, dv, proxy)
+            got = o.pattern_cost(p, C)
+            assert abs(got - want) <= 1e-12 * max(1.0, abs(want)), (proxy, p, got, want)
+
+
+def pin_search_hand_trace(o):
+    """A 4-layer cost matrix worked by hand.  Step 1: S at 1, 2, 3 costs 0.5,
+    0.1, 0.2 -> FFSF.  Step 2: S at 1 makes layers 1 and 2 reuse layer 0
+    (0.5 + 0.9); S at 3 makes layer 3 reuse layer 1 (0.1 + 0.7) -> FFSS, 0.8.
+    Step 3: FSSS = 0.5 + 0.9 + 0.8."""
+    C = np.zeros((4, 4))
+    C[1, 0] = 0.5
+    C[2, 0], C[2, 1] = 0.9, 0.1
+    C[3, 0], C[3, 1], C[3, 2] = 0.8, 0.7, 0.2
+    trace = o.greedy_pattern_search(C, 3)
+    assert [p for p, _ in trace] == ["FFSF", "FFSS", "FSSS"]
+    for (_, c), want in zip(trace, (0.1, 0.8, 2.2)):
+        assert abs(c - want) <= 1e-12
+    assert o.pattern_sources("FSSFSF") == [0, 0, 0, 3, 3, 5]
+
+
+def pin_search_row_constant(o):
+    """If reusing any earlier set costs layer l the same c_l, a pattern costs
+    the sum of c over its S layers, so greedy takes the layers in increasing
+    order of c_l (closed form: a sort), never layer 0."""
+    r = RNG(22)
+    n = 9
+    c = r.permutation(np.linspace(0.1, 2.0, n))
+    C = np.zeros((n, n))
+    for l in range(n):
+        C[l, :l] = c[l]
+    trace = o.greedy_pattern_search(C, n - 1)
+    order = [int(i) for i in np.argsort(c[1:]) + 1]
+    for m, (p, cost) in enumerate(trace, start=1):
+        assert p[0] == "F"
+        assert {i for i, ch in enumerate(p) if ch == "S"} == set(order[:m])
+        assert abs(cost - math.fsum(c[order[:m]])) <= 1e-12
+
+
+def pin_search_bruteforce(o):
+    """Against every pattern of a 7-layer stack with a random cost matrix:
+    one step of greedy reaches the best single conversion (lowest layer on
+    ties), later steps are never better than the best pattern with as many
+    S layers, and each step flips exactly one F layer (never layer 0)."""
+    r = RNG(23)
+    n = 7
+    C = np.tril(r.uniform(0, 1, (n, n)), -1)
+
+    def cost(p):
+        tot, src = 0.0, 0
+        for l, ch in enumerate(p):
+            src = l if ch == "F" else src
+            tot += C[l, src]
+        return tot
+
+    pats = ["F" + "".join(b) for b in itertools.product("FS", repeat=n - 1)]
+    trace = o.greedy_pattern_search(C, n - 1)
+    prev = "F" * n
+    for m, (p, c) in enumerate(trace, start=1):
+        best = min(cost(q) for q in pats if q.count("S") == m)
+        assert c >= best - 1e-12 and abs(c - cost(p)) <= 1e-12
+        if m == 1:
+            first = min((q for q in pats if q.count("S") == 1), key=lambda q: (cost(q), q.index("S")))
+            assert p == first
+        flips = [i for i in range(n) if prev[i] != p[i]]
+        assert len(flips) == 1 and prev[flips[0]] == "F" and flips[0] > 0
+        prev = p
+
+
+def pin_search_identical_keys(o):
+    """Layers sharing one key cache select the same sets: every reuse costs 0
+    under both proxies and greedy converts layers 1, 2, ... in order."""
+    r = RNG(24)
+    layers = _stack_layers(r, 5, shared_keys=True)
+    for proxy in ("output", "miss"):
+        C = o.reuse_costs(layers, [30, 26], 5, 0.4, 8, proxy)
+        assert np.all(C == 0)
+        trace = o.greedy_pattern_search(C, 4)
+        assert [p for p, _ in trace] == ["FSFFF", "FSSFF", "FSSSF", "FSSSS"]
+
+
 ALL_PINS = [
     pin_e4m3_table, pin_e4m3_values, pin_bf16_table,
     pin_indexer_closed_form, pin_indexer_bruteforce, pin_indexer_library,
@@ -428,4 +543,6 @@ ALL_PINS = [
     pin_stack_semantics, pin_stack_identical_keys,
     pin_e4m3_encode_roundtrip, pin_e4m3_encode_bruteforce, pin_e4m3_encode_library,
     pin_bf16_encode_library, pin_fp8_row_quantisation, pin_kv_append,
+    pin_search_cost_decomposition, pin_search_hand_trace, pin_search_row_constant,
+    pin_search_bruteforce, pin_search_identical_keys,
 ]

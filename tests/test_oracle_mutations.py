@@ -162,6 +162,56 @@ def _kv_append_shifted(o):
     return f
 
 
+def _greedy(o, pick_max=False, from_layer=1, tie_high=False):
+    def f(C, n_shared):
+        n = C.shape[0]
+        pattern, trace = ["F"] * n, []
+        for _ in range(n_shared):
+            best, best_c = None, None
+            for l in range(from_layer, n):
+                if pattern[l] != "F":
+                    continue
+                cand = pattern.copy()
+                cand[l] = "S"
+                c = o.pattern_cost("".join(cand), C)
+                better = best_c is None or (c > best_c if pick_max else
+                                            (c <= best_c if tie_high else c < best_c))
+                if better:
+                    best, best_c = cand, c
+            pattern = best
+            trace.append(("".join(pattern), best_c))
+        return trace
+    return f
+
+
+def _sources_previous_layer(o):
+    def f(pattern):
+        o.validate_pattern(pattern, len(pattern))
+        return [l if c == "F" else max(l - 1, 0) for l, c in enumerate(pattern)]
+    return f
+
+
+def _reuse_costs_variant(o, unnormalised=False, transposed=False):
+    orig = o.reuse_costs
+
+    def f(layers, ctx_len, k, scale, d_v, proxy="output", idx_sets=None):
+        if proxy != "output":
+            return orig(layers, ctx_len, k, scale, d_v, proxy, idx_sets)
+        n = len(layers)
+        sets = [o.topk(o.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx_len), ctx_len, k)
+                for L in layers]
+        C = np.zeros((n, n))
+        for l in range(n):
+            for j in range(l):
+                a, b = (j, l) if transposed else (l, j)
+                own = o.sparse_attn(layers[a]["q"], layers[a]["kv"], sets[a], ctx_len, scale, d_v)[0]
+                o2 = o.sparse_attn(layers[a]["q"], layers[a]["kv"], sets[b], ctx_len, scale, d_v)[0]
+                err = float(np.sum((o2 - own) ** 2))
+                C[l, j] = err if unnormalised else err / float(np.sum(own ** 2))
+        return C
+    return f
+
+
 MUTANTS = {
     "indexer_no_relu": ("indexer_scores_row", lambda o: _indexer_row(relu=False)),
     "indexer_w_inside_relu": ("indexer_scores_row", lambda o: _indexer_row(w_inside=True)),
@@ -182,6 +232,12 @@ MUTANTS = {
     "e4m3_encode_subnormal_edge": ("e4m3fn_encode", lambda o: _e4m3_encode(o, normal_from=2.0 ** -7)),
     "fp8_rows_scale_447": ("quantize_fp8_rows_f32", _fp8_rows_scale),
     "kv_append_row_off_by_one": ("kv_append", _kv_append_shifted),
+    "greedy_picks_costliest": ("greedy_pattern_search", lambda o: _greedy(o, pick_max=True)),
+    "greedy_may_share_layer0": ("greedy_pattern_search", lambda o: _greedy(o, from_layer=0)),
+    "greedy_ties_to_higher_layer": ("greedy_pattern_search", lambda o: _greedy(o, tie_high=True)),
+    "search_source_is_previous_layer": ("pattern_sources", _sources_previous_layer),
+    "search_cost_unnormalised": ("reuse_costs", lambda o: _reuse_costs_variant(o, unnormalised=True)),
+    "search_cost_transposed": ("reuse_costs", lambda o: _reuse_costs_variant(o, transposed=True)),
 }
 
 
