@@ -20,6 +20,9 @@ Also reported on the same line:
     every layer (all-F against FSSS): chunked prefill under IndexCache;
   * the KV-cache append (latent bf16 + fp8 indexer key rows) at the decode
     and prefill-chunk shapes, which precedes the path in every step;
+  * the training-free pattern search (greedy F -> S conversion under a proxy
+    loss) on a 48-layer synthetic calibration stack with planted critical
+    layers: device cost-matrix time, host search time, the chosen pattern;
   * the fp64 CPU oracle timed on a bounded sample on this host;
   * the pattern sweep at context 196608 (16 layers, batch 4): all-F, FS,
     FSSS, FSSSSSSS, with the overlap between each S layer's reused index set
@@ -345,6 +348,71 @@ def prefill_stack_bench(dev, n_layers=4, reps=3):
     return out
 
 
+def pattern_search_bench(dev, n_layers=48, n_shared=36):
+    """Training-free pattern search on a synthetic calibration stack with
+    planted structure: layers 0..2 each have an unrelated key cache, layers
+    3..23 share one, layers 24..47 another (an early block and a transition,
+    the layers the pages name as critical).  The device builds the proxy
+    cost matrix (every layer's own index set, every reuse attention, the
+    reductions); the host runs the greedy F -> S search to 75% S layers."""
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    s = gen.Shape(5, "calibration stack", n_layers, "F" * n_layers, B=4, T=1, ctx=32768, H=64,
+                  D=128, idx_dtype="fp8", k=2048, Hq=128)
+    early, transition = 3, 24
+    seg = gen.calibration_segments(n_layers, early, transition)
+    qi = gen.make_indexer_query(s, dev)
+    bases = {g: gen.make_segment_base(s, g, dev) for g in sorted(set(seg))}
+    layers = []
+    for l in range(n_layers):
+        ki = gen.make_indexer_keys(s, l, bases[seg[l]], dev)
+        q, kv = gen.make_mla_layer(s, l, dev)
+        layers.append(dict(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w, k_idx=ki.k,
+                           k_idx_scale=ki.k_scale, q=q, kv=kv,
+                           out=torch.empty((s.B, s.T, s.Hq, s.d_v), dtype=torch.bfloat16,
+                                           device=dev)))
+    del bases
+    ctx = gen.ctx_lens(s, dev)
+    planted = sorted({0} | {l for l in range(1, n_layers) if seg[l] != seg[l - 1]})
+    kw = dict(B=s.B, T=s.T, H=s.H, D=s.D, Lmax=s.Lmax, k=s.k, Hq=s.Hq, idx_dtype=s.idx_dtype,
+              scale=s.scale)
+    out = {"workload": f"{s.name}: {n_layers} layers, batch {s.B}, context {s.ctx}, indexer "
+                       f"{s.H}x{s.D} {s.idx_dtype}, top-{s.k}, MLA {s.Hq} heads; key caches "
+                       f"unrelated across layers {planted}",
+           "planted_critical_layers": planted, "n_shared": n_shared}
+    for proxy in ("output", "miss"):
+        ws = torch.zeros(dsa.reuse_costs_workspace_size(n_layers, proxy=proxy, **kw),
+                         dtype=torch.uint8, device=dev)
+        dsa.reuse_costs(layers, ctx, proxy=proxy, workspace=ws, **kw)   # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cost = dsa.reuse_costs(layers, ctx, proxy=proxy, workspace=ws, **kw)
+        e1.record()
+        e1.synchronize()
+        cost = cost.cpu().numpy()
+        t0 = time.perf_counter()
+        trace = dsa.greedy_search(cost, n_shared)
+        t_host = time.perf_counter() - t0
+        best = trace[-1][0]
+        kept = [l for l, c in enumerate(best) if c == "F"]
+        uniform = gen.tile_pattern("FSSS", n_layers)
+        out[proxy] = dict(cost_matrix_ms=round(e0.elapsed_time(e1), 3),
+                          search_ms=round(t_host * 1e3, 3), pattern=best,
+                          proxy_cost=round(trace[-1][1], 5),
+                          proxy_cost_uniform_fsss=round(dsa.pattern_cost(cost, uniform), 5),
+                          proxy_cost_fixed_12f=round(dsa.pattern_cost(cost, gen.C3_PATTERN), 5),
+                          planted_layers_kept=all(l in kept for l in planted))
+        log(f"pattern search ({proxy}): matrix {out[proxy]['cost_matrix_ms']} ms, search "
+            f"{out[proxy]['search_ms']} ms -> {best} cost {trace[-1][1]:.4f} "
+            f"(uniform FSSS {out[proxy]['proxy_cost_uniform_fsss']:.4f})")
+        del ws, cost
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def kv_append_bench(dev, reps=200):
     """KV-cache append (latent row bf16 + fp8 indexer key with its row scale)
     at the decode shape (batch 8, one token, 131072-row caches) and the prefill
@@ -445,6 +513,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 196K-context pattern sweep")
+    ap.add_argument("--no-search", action="store_true", help="skip the pattern-search leg")
+    ap.add_argument("--search-only", action="store_true",
+                    help="run only the pattern-search leg and print its JSON object")
     ap.add_argument("--kv-append-only", action="store_true",
                     help="run only the KV-cache append leg and print its JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -472,6 +543,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.search_only:
+        print(json.dumps({"pattern_search": pattern_search_bench(dev)}), flush=True)
+        return
     if args.kv_append_only:
         print(json.dumps({"kv_append": kv_append_bench(dev)}), flush=True)
         return
@@ -483,6 +557,7 @@ def main():
     prefill = None if args.no_prefill else prefill_bench(dev)
     prefill_stack = None if args.no_prefill else prefill_stack_bench(dev)
     kv_app = kv_append_bench(dev)
+    search = None if args.no_search else pattern_search_bench(dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(s, layers, args.cpu_seconds)
@@ -516,6 +591,7 @@ def main():
         "prefill": prefill,
         "prefill_stack": prefill_stack,
         "kv_append": kv_app,
+        "pattern_search": search,
         "pattern_sweep": sweep,
     }
     print(json.dumps(line), flush=True)

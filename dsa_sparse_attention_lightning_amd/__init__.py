@@ -9,6 +9,8 @@ must be contiguous device tensors; work is enqueued on torch's current stream.
     sparse_attn(q, kv, idx, ctx_len, scale)                      -> (out, lse)
     kv_append(ctx_len, kv_new, kv_cache, k_new, k_cache, k_scale) -> None (caches in place)
     run_stack(pattern, layers, ...)                              -> stats dict
+    reuse_costs(layers, ctx_len, proxy, ...)                     -> cost [n,n] fp64 (device)
+    pattern_cost(cost, pattern) / greedy_search(cost, n_shared)  -> host-side search
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
 
 __all__ = ["indexer_scores", "topk", "topk_workspace_size", "sparse_attn",
            "sparse_attn_workspace_size", "kv_append", "run_stack",
+           "reuse_costs", "reuse_costs_workspace_size", "pattern_cost", "greedy_search",
            "Stack", "DSAError", "library", "ld_for"]
 
 
@@ -201,6 +204,88 @@ def kv_append(ctx_len, kv_new=None, kv_cache=None, k_new=None, k_cache=None, k_s
                                        _stream(stream)))
 
 
+def _layer_array(layers):
+    arr = (Layer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = Layer(_ptr(L.get("q_idx")), _ptr(L.get("q_idx_scale")), _ptr(L.get("w")),
+                       _ptr(L.get("k_idx")), _ptr(L.get("k_idx_scale")), _ptr(L.get("q")),
+                       _ptr(L.get("kv")), _ptr(L.get("out")), _ptr(L.get("lse")))
+    return arr
+
+
+_PROXIES = {"output": _lib.DSA_PROXY_OUTPUT, "miss": _lib.DSA_PROXY_MISS}
+
+
+def reuse_costs_workspace_size(n_layers: int, *, B, T, H, D, Lmax, k, Hq=0, idx_dtype="bf16",
+                               scale=1.0, proxy="output", d_qk=576, d_v=512) -> int:
+    dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
+    shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale))
+    need = ctypes.c_size_t(0)
+    _lib.check(library().indexcache_reuse_costs_workspace_size(
+        ctypes.byref(shape), n_layers, _PROXIES[proxy], ctypes.byref(need)))
+    return need.value
+
+
+def reuse_costs(layers: Sequence[Dict], ctx_len, *, B, T, H, D, Lmax, k, Hq=0,
+                idx_dtype="bf16", scale=1.0, proxy="output", d_qk=576, d_v=512, workspace=None,
+                stream=None):
+    """Proxy cost matrix [n, n] fp64 (device) of the training-free pattern
+    search: entry (l, j), j < l, is what layer l loses with layer j's index
+    set.  With proxy "output" every layer's `out` receives its all-F output.
+    `workspace`: optional zero-filled uint8 device tensor, reusable."""
+    torch = _torch()
+    if proxy not in _PROXIES:
+        raise ValueError(f"proxy must be one of {sorted(_PROXIES)}")
+    n = len(layers)
+    dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
+    shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale))
+    dev = ctx_len.device
+    need = ctypes.c_size_t(0)
+    lib = library()
+    _lib.check(lib.indexcache_reuse_costs_workspace_size(ctypes.byref(shape), n, _PROXIES[proxy],
+                                                         ctypes.byref(need)))
+    ws = workspace if workspace is not None else torch.zeros(need.value, dtype=torch.uint8,
+                                                             device=dev)
+    ld = ld_for(Lmax)
+    score = torch.empty((B, T, ld), dtype=torch.float32, device=dev)
+    cost = torch.empty((n, n), dtype=torch.float64, device=dev)
+    arr = _layer_array(layers)
+    _lib.check(lib.indexcache_reuse_costs(n, arr, ctypes.byref(shape), _ptr(ctx_len),
+                                          _PROXIES[proxy], _ptr(cost), _ptr(score), ld, _ptr(ws),
+                                          ws.numel(), _stream(stream)))
+    return cost
+
+
+def _host_cost(cost):
+    import numpy as np
+    c = cost.detach().cpu().numpy() if hasattr(cost, "detach") else np.asarray(cost)
+    c = np.ascontiguousarray(c, dtype=np.float64)
+    if c.ndim != 2 or c.shape[0] != c.shape[1]:
+        raise TypeError("cost must be a square [n, n] matrix")
+    return c
+
+
+def pattern_cost(cost, pattern: str) -> float:
+    """Proxy loss of one pattern under a cost matrix (host computation)."""
+    c = _host_cost(cost)
+    out = ctypes.c_double(0.0)
+    _lib.check(library().indexcache_pattern_cost(c.ctypes.data, c.shape[0], pattern.encode(),
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def greedy_search(cost, n_shared: int):
+    """Greedy F -> S conversion: [(pattern, cost)] after each of n_shared steps."""
+    c = _host_cost(cost)
+    n = c.shape[0]
+    pats = ctypes.create_string_buffer(max(1, n_shared * (n + 1)))
+    totals = (ctypes.c_double * max(1, n_shared))()
+    _lib.check(library().indexcache_greedy_search(c.ctypes.data, n, n_shared,
+                                                  ctypes.addressof(pats), ctypes.addressof(totals)))
+    raw = pats.raw
+    return [(raw[m * (n + 1): m * (n + 1) + n].decode(), totals[m]) for m in range(n_shared)]
+
+
 class Stack:
     """Pre-marshalled arguments of indexcache_run_stack for repeated calls."""
 
@@ -210,12 +295,7 @@ class Stack:
         self.pattern = pattern.encode()
         self.n_layers = len(layers)
         self._keep = [layers, ctx_len]
-        arr = (Layer * self.n_layers)()
-        for i, L in enumerate(layers):
-            arr[i] = Layer(_ptr(L.get("q_idx")), _ptr(L.get("q_idx_scale")), _ptr(L.get("w")),
-                           _ptr(L.get("k_idx")), _ptr(L.get("k_idx_scale")), _ptr(L.get("q")),
-                           _ptr(L.get("kv")), _ptr(L.get("out")), _ptr(L.get("lse")))
-        self.layers = arr
+        self.layers = _layer_array(layers)
         dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
         self.shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale))
         self.ctx_len = ctx_len

@@ -11,6 +11,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "dsa_indexcache.h")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 DSA_BF16, DSA_FP8_E4M3 = 0, 1
+DSA_PROXY_OUTPUT, DSA_PROXY_MISS = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 
@@ -50,6 +51,14 @@ SIGNATURES = {
     "indexcache_run_stack": (c_int, [ctypes.c_char_p, c_int, ctypes.POINTER(Layer),
                                      ctypes.POINTER(StackShape), c_vp, c_vp, c_vp, c_i64, c_vp,
                                      ctypes.c_size_t, ctypes.POINTER(StackStats), c_vp]),
+    "indexcache_reuse_costs_workspace_size": (c_int, [ctypes.POINTER(StackShape), c_int, c_int,
+                                                      c_size_p]),
+    "indexcache_reuse_costs": (c_int, [c_int, ctypes.POINTER(Layer), ctypes.POINTER(StackShape),
+                                       c_vp, c_int, c_vp, c_vp, c_i64, c_vp, ctypes.c_size_t,
+                                       c_vp]),
+    "indexcache_pattern_cost": (c_int, [c_vp, c_int, ctypes.c_char_p,
+                                        ctypes.POINTER(ctypes.c_double)]),
+    "indexcache_greedy_search": (c_int, [c_vp, c_int, c_int, c_vp, c_vp]),
 }
 
 _lock = threading.Lock()

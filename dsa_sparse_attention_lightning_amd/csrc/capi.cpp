@@ -57,6 +57,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kMaxTopk = 16384;
 constexpr int kMaxAttnK = 65536;
+constexpr int kMaxSearchK = 8192;  // one row's index list is staged in 32 KB of LDS
 
 dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
                            const float* q_scale, const float* w, const void* k,
@@ -136,6 +137,67 @@ dsa_status_t check_attn(const char* fn, const void* q, const void* kv, const int
 size_t topk_region(const dsa_stack_shape_t* s) {
   const size_t b = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
   return (b + 255) & ~size_t(255);
+}
+
+// One 'F' or 'S' per layer, starting with 'F'.
+dsa_status_t check_pattern(const char* fn, const char* pattern, int n_layers) {
+  CHECK(pattern != nullptr, DSA_ERR_INVALID_ARG, "%s: pattern is NULL", fn);
+  CHECK(n_layers >= 1, DSA_ERR_INVALID_ARG, "%s: n_layers must be >= 1", fn);
+  const size_t plen = strnlen(pattern, (size_t)n_layers + 1);
+  CHECK(plen == (size_t)n_layers, DSA_ERR_INVALID_ARG,
+        "%s: pattern length %zu does not match n_layers %d", fn, plen, n_layers);
+  for (int l = 0; l < n_layers; ++l)
+    CHECK(pattern[l] == 'F' || pattern[l] == 'S', DSA_ERR_INVALID_ARG,
+          "%s: pattern[%d] = '%c' is neither 'F' nor 'S'", fn, l, pattern[l]);
+  CHECK(pattern[0] == 'F', DSA_ERR_INVALID_ARG,
+        "%s: pattern must start with 'F' (an S layer reuses the nearest preceding F)", fn);
+  return DSA_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Workspace of the cost-matrix builder, in order: the top-k region (kept
+// zero between calls), the attention region, the n index sets, one
+// attention output for the reused sets, the reduction partials.
+struct ReuseLayout {
+  size_t attn, attn_bytes, sets, tmp, partials, total;
+};
+
+ReuseLayout reuse_layout(const dsa_stack_shape_t* s, int n, bool output) {
+  ReuseLayout L;
+  size_t off = topk_region(s);
+  L.attn = off;
+  L.attn_bytes = output ? dsa::sparse_attn_workspace_bytes(s->B, s->T, s->Hq, s->k, s->d_v) : 0;
+  off += align256(L.attn_bytes);
+  L.sets = off;
+  off += align256((size_t)n * s->B * s->T * s->k * sizeof(int32_t));
+  L.tmp = off;
+  if (output) off += align256((size_t)s->B * s->T * s->Hq * s->d_v * 2);
+  L.partials = off;
+  off += align256((size_t)dsa::kReuseCostMaxGrid * sizeof(double2));
+  L.total = off;
+  return L;
+}
+
+// Proxy loss of a validated pattern: sum over layers, in order, of
+// C[l][src(l)], src(l) the nearest F layer at or before l.
+double pattern_total(const double* C, int n, const char* p) {
+  double t = 0.0;
+  int src = 0;
+  for (int l = 0; l < n; ++l) {
+    if (p[l] == 'F') src = l;
+    t += C[(size_t)l * n + src];
+  }
+  return t;
+}
+
+dsa_status_t check_cost_matrix(const char* fn, const double* C, int n) {
+  CHECK(C != nullptr, DSA_ERR_INVALID_ARG, "%s: cost is NULL", fn);
+  CHECK(n >= 1 && n <= 4096, DSA_ERR_INVALID_ARG, "%s: n_layers must be in 1..4096 (got %d)",
+        fn, n);
+  for (size_t i = 0; i < (size_t)n * n; ++i)
+    CHECK(C[i] == C[i], DSA_ERR_INVALID_ARG, "%s: cost[%zu] is NaN", fn, i);
+  return DSA_OK;
 }
 
 bool uses_prefill_indexer(int T, int H, int D) { return T > 1 && dsa::indexer_prefill_supported(H, D); }
@@ -296,15 +358,10 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
   const char* fn = "indexcache_run_stack";
   CHECK(pattern != nullptr && layers != nullptr && shape != nullptr, DSA_ERR_INVALID_ARG,
         "%s: pattern, layers and shape must be non-NULL", fn);
-  CHECK(n_layers >= 1, DSA_ERR_INVALID_ARG, "%s: n_layers must be >= 1", fn);
-  const size_t plen = strnlen(pattern, (size_t)n_layers + 1);
-  CHECK(plen == (size_t)n_layers, DSA_ERR_INVALID_ARG,
-        "%s: pattern length %zu does not match n_layers %d", fn, plen, n_layers);
-  for (int l = 0; l < n_layers; ++l)
-    CHECK(pattern[l] == 'F' || pattern[l] == 'S', DSA_ERR_INVALID_ARG,
-          "%s: pattern[%d] = '%c' is neither 'F' nor 'S'", fn, l, pattern[l]);
-  CHECK(pattern[0] == 'F', DSA_ERR_INVALID_ARG,
-        "%s: pattern must start with 'F' (an S layer reuses the nearest preceding F)", fn);
+  {
+    dsa_status_t st = check_pattern(fn, pattern, n_layers);
+    if (st != DSA_OK) return st;
+  }
   const dsa_stack_shape_t& s = *shape;
   CHECK(s.Hq >= 0, DSA_ERR_INVALID_ARG, "%s: Hq must be >= 0", fn);
   size_t need = 0;
@@ -369,6 +426,160 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
     }
   }
   if (stats) *stats = st_local;
+  return ok();
+}
+
+dsa_status_t indexcache_reuse_costs_workspace_size(const dsa_stack_shape_t* s, int n_layers,
+                                                   dsa_reuse_proxy_t proxy, size_t* bytes) {
+  const char* fn = "indexcache_reuse_costs_workspace_size";
+  CHECK(s != nullptr && bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: NULL argument", fn);
+  CHECK(n_layers >= 1, DSA_ERR_INVALID_ARG, "%s: n_layers must be >= 1", fn);
+  CHECK(proxy == DSA_PROXY_OUTPUT || proxy == DSA_PROXY_MISS, DSA_ERR_INVALID_ARG,
+        "%s: unknown proxy %d", fn, (int)proxy);
+  CHECK(s->B >= 1 && s->T >= 1 && s->Lmax >= 1 && s->k >= 1, DSA_ERR_INVALID_ARG,
+        "%s: bad sizes", fn);
+  CHECK(s->k <= kMaxSearchK, DSA_ERR_UNSUPPORTED, "%s: k (%d) above %d", fn, s->k, kMaxSearchK);
+  if (proxy == DSA_PROXY_OUTPUT)
+    CHECK(s->Hq >= 16 && s->Hq % 16 == 0 && s->d_v == 512, DSA_ERR_INVALID_ARG,
+          "%s: the output proxy needs attention sizes (Hq a multiple of 16, d_v 512)", fn);
+  *bytes = reuse_layout(s, n_layers, proxy == DSA_PROXY_OUTPUT).total;
+  return ok();
+}
+
+dsa_status_t indexcache_reuse_costs(int n_layers, const dsa_layer_t* layers,
+                                    const dsa_stack_shape_t* shape, const int32_t* ctx_len,
+                                    dsa_reuse_proxy_t proxy, double* cost, float* score_buf,
+                                    int64_t ld_scores, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  const char* fn = "indexcache_reuse_costs";
+  CHECK(layers != nullptr && shape != nullptr, DSA_ERR_INVALID_ARG,
+        "%s: layers and shape must be non-NULL", fn);
+  size_t need = 0;
+  {
+    dsa_status_t st = indexcache_reuse_costs_workspace_size(shape, n_layers, proxy, &need);
+    if (st != DSA_OK) return st;
+  }
+  CHECK(workspace_bytes >= need, DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given",
+        fn, need, workspace_bytes);
+  CHECK_PTR(workspace);
+  CHECK_PTR(cost);
+  const dsa_stack_shape_t& s = *shape;
+  const bool output = proxy == DSA_PROXY_OUTPUT;
+  const ReuseLayout W = reuse_layout(shape, n_layers, output);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  int32_t* sets = reinterpret_cast<int32_t*>(ws + W.sets);
+  char what[96];
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    snprintf(what, sizeof(what), "%s (layer %d)", fn, l);
+    dsa_status_t st = check_indexer(what, L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
+                                    L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
+                                    score_buf, ld_scores);
+    if (st != DSA_OK) return st;
+    st = check_topk(what, score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k, sets);
+    if (st != DSA_OK) return st;
+    if (output) {
+      st = check_attn(what, L.q, L.kv, sets, ctx_len, s.B, s.T, s.Hq, s.Lmax, s.k, s.d_qk, s.d_v,
+                      s.scale, L.out, L.lse);
+      if (st != DSA_OK) return st;
+    }
+  }
+  const int64_t rows = (int64_t)s.B * s.T;
+  const size_t set_elems = (size_t)rows * s.k;
+  const int64_t out_elems = rows * s.Hq * s.d_v;
+  const size_t tk_bytes = topk_region(shape);
+  void* attn_ws = W.attn_bytes ? ws + W.attn : nullptr;
+  void* tmp = ws + W.tmp;
+  double2* partials = reinterpret_cast<double2*>(ws + W.partials);
+  uint32_t* row_hist = uses_prefill_indexer(s.T, s.H, s.D)
+                           ? nullptr
+                           : dsa::topk_row_hist(workspace, s.B, s.T, s.Lmax, s.k);
+  dsa_status_t st =
+      hip_status(dsa::launch_fill_zero_f64(cost, (int64_t)n_layers * n_layers, stream),
+                 "cost fill launch");
+  if (st != DSA_OK) return st;
+  // Every layer's own index set.
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    st = run_indexer(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx, L.k_idx_scale, ctx_len,
+                     s.B, s.T, s.H, s.D, s.Lmax, score_buf, ld_scores, row_hist, stream);
+    if (st != DSA_OK) return st;
+    st = hip_status(dsa::launch_topk(score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k,
+                                     sets + l * set_elems, workspace, tk_bytes,
+                                     row_hist != nullptr, stream),
+                    "topk launch");
+    if (st != DSA_OK) return st;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    const int32_t* own = sets + l * set_elems;
+    if (output) {
+      st = hip_status(dsa::launch_sparse_attn(L.q, L.kv, own, ctx_len, s.B, s.T, s.Hq, s.Lmax,
+                                              s.k, s.scale, L.out, L.lse, attn_ws, W.attn_bytes,
+                                              stream),
+                      "sparse attention launch");
+      if (st != DSA_OK) return st;
+    }
+    for (int j = 0; j < l; ++j) {
+      const int32_t* reused = sets + j * set_elems;
+      double* dst = cost + (size_t)l * n_layers + j;
+      if (output) {
+        st = hip_status(dsa::launch_sparse_attn(L.q, L.kv, reused, ctx_len, s.B, s.T, s.Hq,
+                                                s.Lmax, s.k, s.scale, tmp, nullptr, attn_ws,
+                                                W.attn_bytes, stream),
+                        "sparse attention launch");
+        if (st != DSA_OK) return st;
+        st = hip_status(dsa::launch_output_cost(tmp, L.out, out_elems, partials, dst, stream),
+                        "output cost launch");
+      } else {
+        st = hip_status(dsa::launch_miss_cost(reused, own, rows, s.k, partials, dst, stream),
+                        "miss cost launch");
+      }
+      if (st != DSA_OK) return st;
+    }
+  }
+  return ok();
+}
+
+dsa_status_t indexcache_pattern_cost(const double* cost, int n_layers, const char* pattern,
+                                     double* total) {
+  const char* fn = "indexcache_pattern_cost";
+  CHECK(total != nullptr, DSA_ERR_INVALID_ARG, "%s: total is NULL", fn);
+  dsa_status_t st = check_cost_matrix(fn, cost, n_layers);
+  if (st != DSA_OK) return st;
+  st = check_pattern(fn, pattern, n_layers);
+  if (st != DSA_OK) return st;
+  *total = pattern_total(cost, n_layers, pattern);
+  return ok();
+}
+
+dsa_status_t indexcache_greedy_search(const double* cost, int n_layers, int n_shared,
+                                      char* patterns, double* totals) {
+  const char* fn = "indexcache_greedy_search";
+  dsa_status_t st = check_cost_matrix(fn, cost, n_layers);
+  if (st != DSA_OK) return st;
+  CHECK(n_shared >= 0 && n_shared < n_layers, DSA_ERR_INVALID_ARG,
+        "%s: n_shared must be in 0..%d (got %d)", fn, n_layers - 1, n_shared);
+  CHECK(n_shared == 0 || (patterns != nullptr && totals != nullptr), DSA_ERR_INVALID_ARG,
+        "%s: patterns and totals must be non-NULL", fn);
+  std::string p((size_t)n_layers, 'F');
+  for (int m = 0; m < n_shared; ++m) {
+    int best = -1;
+    double best_cost = 0.0;
+    for (int l = 1; l < n_layers; ++l) {
+      if (p[l] != 'F') continue;
+      p[l] = 'S';
+      const double c = pattern_total(cost, n_layers, p.c_str());
+      p[l] = 'F';
+      if (best < 0 || c < best_cost) {
+        best = l;
+        best_cost = c;
+      }
+    }
+    p[best] = 'S';
+    memcpy(patterns + (size_t)m * (n_layers + 1), p.c_str(), (size_t)n_layers + 1);
+    totals[m] = best_cost;
+  }
   return ok();
 }
 

@@ -47,4 +47,17 @@ hipError_t launch_kv_append(const float* kv_new, const float* k_new, const int32
                             int B, int T, int Lmax, int d_qk, int D, bool k_fp8, void* kv_cache,
                             void* k_cache, float* k_scale, hipStream_t stream);
 
+// Pattern-search proxy costs.  Each writes one fp64 value to *dst (device)
+// after a reduction whose per-workgroup partials go to `partials`, which
+// must hold kReuseCostMaxGrid entries.
+constexpr int kReuseCostMaxGrid = 1024;
+hipError_t launch_fill_zero_f64(double* p, int64_t n, hipStream_t stream);
+// sum (out - ref)^2 / sum ref^2 over `elems` bf16 values (elems % 8 == 0).
+hipError_t launch_output_cost(const void* out, const void* ref, int64_t elems, double2* partials,
+                              double* dst, hipStream_t stream);
+// 1 - sum |reused ∩ own| / sum |own| over `rows` index lists of length
+// k <= 8192 (a row is staged in LDS).
+hipError_t launch_miss_cost(const int32_t* reused, const int32_t* own, int64_t rows, int k,
+                            double2* partials, double* dst, hipStream_t stream);
+
 }  // namespace dsa

@@ -151,6 +151,19 @@ def make_indexer_keys(s: Shape, layer: int, k_base: torch.Tensor, device="cpu",
     return IndexerKeys(k, ks)
 
 
+def calibration_segments(n_layers: int, early: int, transition: int) -> List[int]:
+    """Key-cache segment of each layer for a stack with planted structure:
+    layers 0..early-1 each have a segment of their own, layers early..
+    transition-1 share one, layers transition.. share another."""
+    return [l if l < early else (early if l < transition else early + 1)
+            for l in range(n_layers)]
+
+
+def make_segment_base(s: Shape, segment: int, device="cpu") -> torch.Tensor:
+    """Key base of one segment (segment 0 is the stack's usual key base)."""
+    return randn((s.B, s.Lmax, s.D), seed_of(s.cfg_id, segment, "k_base"), device)
+
+
 def make_mla_layer(s: Shape, layer: int, device="cpu"):
     """(q [B,T,Hq,d_qk] bf16, kv [B,Lmax,d_qk] bf16) for one layer."""
     q = randn((s.B, s.T, s.Hq, s.d_qk), seed_of(s.cfg_id, layer, "q"), device).to(torch.bfloat16)

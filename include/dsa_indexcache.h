@@ -14,8 +14,9 @@
  *    preceding F layer - one conditional branch in the inference loop.
  *
  * Conventions shared by every entry point
- *  - All pointers except `pattern`, `layers`, `shape`, `stats` and the size
- *    outputs are DEVICE pointers, 16-byte aligned, rows contiguous.  The
+ *  - All pointers except `pattern`, `layers`, `shape`, `stats`, the size
+ *    outputs and the arguments of the host-only search helpers are DEVICE
+ *    pointers, 16-byte aligned, rows contiguous.  The
  *    caller owns every buffer; the library never allocates, frees or
  *    synchronises.  Work is enqueued on `stream` (0 = the null stream) and is
  *    complete when the caller synchronises that stream.
@@ -216,6 +217,66 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
                                   int32_t* idx_buf, float* score_buf, int64_t ld_scores,
                                   void* workspace, size_t workspace_bytes,
                                   dsa_stack_stats_t* stats, hipStream_t stream);
+
+/*
+ * Training-free pattern search (technical summary §2, part A of the two
+ * configuration approaches: start from all-F and convert, one layer at a
+ * time, the layer whose switch to S raises the calibration loss least).
+ * Without a trained model the loss is a PROXY, built from a cost matrix:
+ *
+ *   cost[l*n + j], j < l: what layer l loses by attending with layer j's
+ *   index set T_j instead of its own T_l (T = top-k of the layer's indexer);
+ *     DSA_PROXY_OUTPUT: sum (o_l[T_j] - o_l[T_l])^2 / sum o_l[T_l]^2 over
+ *       layer l's bf16 attention outputs (0/0 = 0, x/0 = +inf);
+ *     DSA_PROXY_MISS:   1 - sum_rows |T_j ∩ T_l| / sum_rows |T_l|
+ *       (0 when no row selects anything);
+ *   cost[l*n + j] = 0 for j >= l.
+ *   The cost of a pattern is sum over l, in layer order, of cost[l*n + src(l)]
+ *   with src(l) the nearest F layer at or before l.
+ */
+typedef enum dsa_reuse_proxy {
+  DSA_PROXY_OUTPUT = 0,
+  DSA_PROXY_MISS = 1
+} dsa_reuse_proxy_t;
+
+/*
+ * Cost matrix of a layer stack on the device.  Every layer is scored as an F
+ * layer (indexer inputs are read on all layers).  cost: DEVICE [n_layers *
+ * n_layers] fp64, row-major, fully written.  score_buf / ld_scores as for
+ * indexcache_run_stack.  DSA_PROXY_OUTPUT needs shape->Hq > 0 and every
+ * layer's q, kv and out: on return layers[l].out (and lse when non-NULL)
+ * holds layer l's attention output over its own set, i.e. the all-F output.
+ * DSA_PROXY_MISS reads no attention inputs (Hq is ignored).  k <= 8192.  The workspace
+ * (indexcache_reuse_costs_workspace_size bytes) holds the n_layers index sets
+ * and the reduction scratch; like the stack's, it must be zero-filled before
+ * its first use and is left that way.  Work: n_layers indexer + top-k runs,
+ * plus n_layers*(n_layers+1)/2 sparse attention runs for DSA_PROXY_OUTPUT.
+ */
+dsa_status_t indexcache_reuse_costs_workspace_size(const dsa_stack_shape_t* shape, int n_layers,
+                                                   dsa_reuse_proxy_t proxy, size_t* bytes);
+dsa_status_t indexcache_reuse_costs(int n_layers, const dsa_layer_t* layers,
+                                    const dsa_stack_shape_t* shape, const int32_t* ctx_len,
+                                    dsa_reuse_proxy_t proxy, double* cost, float* score_buf,
+                                    int64_t ld_scores, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * Host-only helpers over a HOST copy of the cost matrix (entries finite or
+ * +inf; NaN is rejected).  Both run on the calling thread and touch no GPU.
+ *
+ * indexcache_pattern_cost: the proxy loss of one pattern (validated like
+ * indexcache_run_stack's).
+ *
+ * indexcache_greedy_search: starting from all-F, each of n_shared steps
+ * (0 <= n_shared < n_layers) tries every F layer but layer 0 as S and keeps
+ * the conversion with the lowest pattern cost, the lower layer on equal cost.
+ * patterns: n_shared * (n_layers + 1) chars, row m receiving the
+ * NUL-terminated pattern after step m + 1; totals: n_shared doubles, its cost.
+ */
+dsa_status_t indexcache_pattern_cost(const double* cost, int n_layers, const char* pattern,
+                                     double* total);
+dsa_status_t indexcache_greedy_search(const double* cost, int n_layers, int n_shared,
+                                      char* patterns, double* totals);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,158 @@
+"""Pattern-search cost matrix on the GPU against the oracle (GPU).
+
+The device builds every layer's own index set, runs the reuse attentions
+and reduces the proxies; the oracle recomputes the matrix from the same
+index sets (checked separately against its own top-k with the k-th boundary
+rule).  The miss proxy is integer counting followed by one division, so it
+must match bit for bit.  The output proxy compares bf16 outputs: with every
+output rounded once to bf16 (relative error at most 2^-9 per element), the
+error vector of a difference of two outputs has norm at most eta = 2^-7 of
+the reference norm, so a cost C moves by at most 2*sqrt(C)*eta + eta^2 + C*2^-7
+(numerator and denominator perturbations); that bound is the tolerance.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dsa_sparse_attention_lightning_amd as dsa
+from dsa_sparse_attention_lightning_amd import inputs as gen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ETA = 2.0 ** -7
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def build_stack(n_layers, B, T, ctx, H, D, dtype, k, Hq, early, transition, seed):
+    s = gen.Shape(seed, "search", n_layers, "F" * n_layers, B=B, T=T, ctx=max(ctx), H=H, D=D,
+                  idx_dtype=dtype, k=k, Hq=Hq)
+    qi = gen.make_indexer_query(s, DEV)
+    seg = gen.calibration_segments(n_layers, early, transition)
+    bases = {g: gen.make_segment_base(s, g, DEV) for g in sorted(set(seg))}
+    layers = []
+    for l in range(n_layers):
+        ki = gen.make_indexer_keys(s, l, bases[seg[l]], DEV)
+        L = dict(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w, k_idx=ki.k, k_idx_scale=ki.k_scale)
+        if Hq:
+            q, kv = gen.make_mla_layer(s, l, DEV)
+            L.update(q=q, kv=kv,
+                     out=torch.empty((B, T, Hq, s.d_v), dtype=torch.bfloat16, device=DEV),
+                     lse=torch.empty((B, T, Hq), dtype=torch.float32, device=DEV))
+        layers.append(L)
+    return s, layers, seg, gen.ctx_lens(s, DEV, ctx)
+
+
+def kw(s):
+    return dict(B=s.B, T=s.T, H=s.H, D=s.D, Lmax=s.Lmax, k=s.k, Hq=s.Hq,
+                idx_dtype=s.idx_dtype, scale=s.scale)
+
+
+def gpu_sets(s, layers, ctx_t, ctx, check_against_oracle=True):
+    """Each layer's own set through the standalone kernels (the cost builder
+    runs the same kernels), checked against the oracle's top-k."""
+    sets = []
+    for L in layers:
+        sc = dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx_t, L["q_idx_scale"],
+                                L["k_idx_scale"])
+        idx = dsa.topk(sc, ctx_t, s.k).cpu().numpy()
+        if check_against_oracle:
+            ref = oracle.indexer_scores(parity.host_real(L["q_idx"], L["q_idx_scale"]),
+                                        L["w"].cpu().double().numpy(),
+                                        parity.host_real(L["k_idx"], L["k_idx_scale"]), ctx)
+            parity.check_topk_boundary(idx, ref, ctx, s.k)
+        sets.append(idx)
+    return sets
+
+
+def host_layers(layers):
+    return [dict(q=parity.host_real(L["q"]), kv=parity.host_real(L["kv"])) for L in layers]
+
+
+CASES = [
+    # n, B, T, ctx, H, D, dtype, k, Hq, early, transition
+    (6, 2, 1, [900, 1300], 16, 64, "bf16", 128, 16, 2, 4),
+    (5, 1, 3, [2100], 32, 128, "fp8", 256, 32, 1, 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"n{c[0]}B{c[1]}T{c[2]}{c[6]}k{c[7]}")
+def test_output_cost_matrix(case):
+    n, B, T, ctx, H, D, dtype, k, Hq, early, trans = case
+    say("reuse costs (output proxy)", case)
+    s, layers, _, ctx_t = build_stack(n, B, T, ctx, H, D, dtype, k, Hq, early, trans, seed=31)
+    cost = dsa.reuse_costs(layers, ctx_t, proxy="output", **kw(s))
+    torch.cuda.synchronize()
+    got = cost.cpu().numpy()
+    sets = gpu_sets(s, layers, ctx_t, ctx)
+    hl = host_layers(layers)
+    ref = oracle.reuse_costs(hl, ctx, k, s.scale, s.d_v, "output", idx_sets=sets)
+    assert np.all(got[np.triu_indices(n)] == 0)
+    tol = 2 * np.sqrt(ref) * ETA + ETA ** 2 + ref * 2.0 ** -7
+    low = np.tril_indices(n, -1)
+    bad = np.abs(got[low] - ref[low]) > tol[low]
+    assert not bad.any(), f"cost mismatch: gpu {got[low][bad]} oracle {ref[low][bad]}"
+    # each layer's out holds its all-F output
+    for l in range(n):
+        o, z = oracle.sparse_attn(hl[l]["q"], hl[l]["kv"], sets[l], ctx, s.scale, s.d_v)
+        parity.check_attn(layers[l]["out"].float().cpu().numpy(), layers[l]["lse"].cpu().numpy(),
+                          o, z)
+    say("cost range", float(ref[low].min()), float(ref[low].max()))
+
+
+@pytest.mark.parametrize("dtype,T,ctx,k", [("fp8", 1, [700, 3000, 2049], 2048),
+                                           ("bf16", 5, [300, 4100], 512)],
+                         ids=["decode-ragged-short-rows", "prefill-rows"])
+def test_miss_cost_matrix_exact(dtype, T, ctx, k):
+    """Rows with fewer visible positions than k (-1 padded) included."""
+    n = 7
+    say("reuse costs (miss proxy)", dtype, T, ctx, k)
+    s, layers, _, ctx_t = build_stack(n, len(ctx), T, ctx, 64, 128, dtype, k, 0, 2, 4, seed=32)
+    cost = dsa.reuse_costs(layers, ctx_t, proxy="miss", **kw(s))
+    torch.cuda.synchronize()
+    got = cost.cpu().numpy()
+    sets = gpu_sets(s, layers, ctx_t, ctx)
+    ref = oracle.reuse_costs([{}] * n, ctx, k, s.scale, s.d_v, "miss", idx_sets=sets)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), (got, ref)
+
+
+def test_search_finds_planted_layers():
+    """A stack whose first two layers and the start of two later segments
+    have unrelated key caches: four greedy steps convert exactly the other
+    four layers, under both proxies, and the device-matrix search equals the
+    oracle's search on the same matrix."""
+    n = 8
+    say("planted search")
+    s, layers, seg, ctx_t = build_stack(n, 2, 1, [4096, 3000], 32, 128, "fp8", 256, 16, 2, 5,
+                                        seed=33)
+    starts = {l for l in range(n) if l == 0 or seg[l] != seg[l - 1]}
+    assert starts == {0, 1, 2, 5}
+    for proxy in ("output", "miss"):
+        cost = dsa.reuse_costs(layers, ctx_t, proxy=proxy, **kw(s)).cpu().numpy()
+        trace = dsa.greedy_search(cost, 4)
+        assert trace == oracle.greedy_pattern_search(cost, 4)
+        final = trace[-1][0]
+        assert {l for l, c in enumerate(final) if c == "F"} == starts, (proxy, final)
+        assert dsa.pattern_cost(cost, final) == trace[-1][1]
+        say(proxy, [p for p, _ in trace])
+
+
+def test_cost_matrix_is_deterministic():
+    """Two calls on one reused workspace give the same bits (the workspace's
+    top-k region is left zero-filled by every call)."""
+    say("determinism")
+    s, layers, _, ctx_t = build_stack(4, 2, 1, [1500, 1500], 16, 64, "bf16", 128, 16, 1, 2,
+                                      seed=34)
+    need = dsa.reuse_costs_workspace_size(proxy="output", n_layers=4, **kw(s))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    a = dsa.reuse_costs(layers, ctx_t, proxy="output", workspace=ws, **kw(s)).cpu().numpy()
+    b = dsa.reuse_costs(layers, ctx_t, proxy="output", workspace=ws, **kw(s)).cpu().numpy()
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
