@@ -29,7 +29,7 @@ Also reported on the same line:
     and the set its own indexer would select.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
-                [--no-sweep]
+                [--no-sweep] [--no-search] [--no-kv-append] [--search-only] [--kv-append-only]
 """
 from __future__ import annotations
 
@@ -514,6 +514,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 196K-context pattern sweep")
     ap.add_argument("--no-search", action="store_true", help="skip the pattern-search leg")
+    ap.add_argument("--no-kv-append", action="store_true", help="skip the KV-append leg")
     ap.add_argument("--search-only", action="store_true",
                     help="run only the pattern-search leg and print its JSON object")
     ap.add_argument("--kv-append-only", action="store_true",
@@ -556,7 +557,7 @@ def main():
         sweep = pattern_sweep(dev, max(5, args.steps // 3), 2)
     prefill = None if args.no_prefill else prefill_bench(dev)
     prefill_stack = None if args.no_prefill else prefill_stack_bench(dev)
-    kv_app = kv_append_bench(dev)
+    kv_app = None if args.no_kv_append else kv_append_bench(dev)
     search = None if args.no_search else pattern_search_bench(dev)
     cpu = None
     if not args.no_cpu_baseline:
