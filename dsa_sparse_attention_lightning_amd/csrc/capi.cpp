@@ -57,7 +57,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kMaxTopk = 16384;
 constexpr int kMaxAttnK = 65536;
-constexpr int kMaxSearchK = 8192;  // one row's index list is staged in 32 KB of LDS
+constexpr int kMaxSearchK = 8192;
+// Kernels address one sequence's cache through a buffer resource with a
+// 32-bit byte range.
+constexpr int64_t kMaxSeqBytes = 2147483647LL;  // one row's index list is staged in 32 KB of LDS
 
 dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
                            const float* q_scale, const float* w, const void* k,
@@ -72,6 +75,9 @@ dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
         (long long)B * T);
   CHECK(D == 64 || D == 128, DSA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
   CHECK(H >= 1 && H <= 64, DSA_ERR_UNSUPPORTED, "%s: H must be in 1..64 (got %d)", fn, H);
+  CHECK((int64_t)Lmax * D * (dtype == DSA_BF16 ? 2 : 1) <= kMaxSeqBytes, DSA_ERR_UNSUPPORTED,
+        "%s: one sequence's key cache (Lmax %d x D %d) exceeds %lld bytes", fn, Lmax, D,
+        (long long)kMaxSeqBytes);
   CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
         "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
         Lmax);

@@ -14,13 +14,21 @@
 //
 // Each wave streams 8 KB key tiles (64 fp8 or 32 bf16 rows of D = 128), the
 // waves of a row interleaved tile by tile, with fully coalesced 16-byte
-// loads, three tiles in flight,
-// and regroups each tile through its own LDS region so that lane l holds
-// D*e/2 contiguous bytes of key (l & 31).  The epilogue applies ReLU and the
-// per-head weight w' = w (bf16) or w * q_scale (fp8: the positive per-row
-// scales commute with the ReLU) and sums the heads: 16 rows per lane in
-// registers, the other 16 in lane l ^ 32.  Lanes 0..31 then store 32
-// consecutive fp32 scores (times the key's scale for fp8) or -inf past pos.
+// loads, three tiles in flight, and regroups each tile through its own LDS
+// region so that lane l holds D*e/2 contiguous bytes of key (l & 31).  (Loads
+// straight into that layout touch 32 partial cache lines per instruction and
+// run far slower.)  Keys, scales and scores go through buffer resources with
+// a per-lane constant offset and a scalar per-tile offset, so the stream costs
+// no vector address arithmetic, and the resource bounds replace clamping: a
+// key past Lmax reads as zero and its score store is dropped.  The epilogue
+// applies ReLU (a signed-integer max on the bit pattern: negative floats,
+// -0 included, have negative patterns) and the per-head weight w' = w (bf16)
+// or w * q_scale (fp8: the positive per-row scales commute with the ReLU) and
+// sums the heads: 16 rows per lane in registers in four independent chains,
+// the other 16 in lane l ^ 32.  Lanes 0..31 then store 32 consecutive fp32
+// scores (times the key's scale for fp8) or -inf past pos.  The launch bound
+// of two workgroups per CU caps a wave at 256 registers, which keeps the MFMA
+// accumulators in VGPRs where the epilogue reads them.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -32,9 +40,14 @@ constexpr int kDecWaves = 4;
 constexpr int kTileBytes = 8192;   // key bytes per wave step
 constexpr int kHistBits = 12;      // first radix digit of the top-k selection
 constexpr int kHistBins = 1 << kHistBits;
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9; cache
+// policy 2 marks a load nontemporal.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNT = 2;
+constexpr int kParts = 4;  // independent fma chains of the head sum
 
 template <int D, bool FP8, int HB>
-__global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
+__global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
@@ -53,7 +66,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   __shared__ uint32_t lhist[kHistBins];  // used when row_hist is given
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 5;
   const int col = lane & 31;
   const int row = blockIdx.y;  // b * T + t
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
     for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
     __syncthreads();
   }
-  auto tmap = [&](int j) { return first + j * wstride; };
+  auto tmap = [&](int j) { return __builtin_amdgcn_readfirstlane(first + j * wstride); };
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
@@ -110,17 +123,24 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
   // multiplied (the loop is unrolled by three so every buffer is static).
   i32x4 ba[NL], bb[NL], bc[NL];
   float sa[CB], sb[CB], sc_[CB];
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kbase, 0, Lmax * ROWB, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(FP8 ? ksb : k_scale), 0, FP8 ? Lmax * 4 : 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)srow, 0, Lmax * 4, kBufferWord3);
   auto load = [&](int seq, i32x4(&buf)[NL], float(&bs)[CB]) {
     const int tile = tmap(seq);
 #pragma unroll
-    for (int v = 0; v < NL; ++v) {
-      const int off = 16 * lane + 1024 * v;  // byte offset in the tile
-      const int key = min(tile * TK + off / ROWB, Lmax - 1);
-      buf[v] = ld16_nt(kbase + (int64_t)key * ROWB + (off % ROWB));
-    }
+    for (int v = 0; v < NL; ++v)
+      buf[v] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             kr, 16 * lane + 1024 * (v & 3),
+                                             tile * kTileBytes + 4096 * (v >> 2), kNT));
     if (FP8) {
 #pragma unroll
-      for (int c = 0; c < CB; ++c) bs[c] = ksb[min(tile * TK + c * 32 + col, Lmax - 1)];
+      for (int c = 0; c < CB; ++c)
+        bs[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              sr, col * 4, (tile * TK + c * 32) * 4, kNT));
     }
   };
   auto compute = [&](int seq, const i32x4(&raw)[NL], const float(&cs)[CB]) {
@@ -162,21 +182,31 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
           }
         }
       }
-      float sc = 0.f;
+      float part[kParts];
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) part[p] = 0.f;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc = fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), sc);
-      sc += __shfl_xor(sc, 32, kWave);
-      const int key = tile * TK + c * 32 + col;
-      if (g == 0 && key < Lmax) {
-        float o = -INFINITY;
-        if (key <= pos) {
-          o = FP8 ? sc * cs[c] : sc;
-          // top-k histogram: top 12 bits of the order-preserving key
-          if (row_hist) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);
+        for (int r = 0; r < 16; ++r) {
+          const float x = __int_as_float(max(__float_as_int(acc[hb][r]), 0));
+          part[(hb * 16 + r) % kParts] = fmaf(wv[hb][r], x, part[(hb * 16 + r) % kParts]);
         }
-        srow[key] = o;
+      float sc = part[0];
+#pragma unroll
+      for (int p = 1; p < kParts; ++p) sc += part[p];
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc),
+                                                   false, false);
+        sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      const int key = tile * TK + c * 32 + col;
+      const bool vis = key <= pos && key < Lmax;
+      const float o = vis ? (FP8 ? sc * cs[c] : sc) : -INFINITY;
+      if (g == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, col * 4,
+                                              (tile * TK + c * 32) * 4, 0);
+        if (row_hist && vis) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -204,7 +234,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void indexer_decode_kernel(
 }
 
 #ifndef DSA_DEC_WG_TARGET
-#define DSA_DEC_WG_TARGET 512
+#define DSA_DEC_WG_TARGET 256
 #endif
 
 template <int D, bool FP8, int HB>
@@ -215,7 +245,7 @@ hipError_t launch_dec(const void* q, const float* q_scale, const float* w, const
   const int rows = B * T;
   const int tk = kTileBytes / (D * (FP8 ? 1 : 2));
   const int tiles = (Lmax + tk - 1) / tk;
-  // Few long-lived waves (about 2 workgroups per CU), each taking many key
+  // Few long-lived waves (about one workgroup per CU), each taking many key
   // tiles, so that its query fragments are loaded once.
   int64_t want_waves = (int64_t)DSA_DEC_WG_TARGET * kDecWaves;
   int tpw = (int)(((int64_t)rows * tiles + want_waves - 1) / want_waves);

@@ -77,8 +77,9 @@ const char* dsa_version(void);
  * k_scale  [B,Lmax] fp32 per-row scale (> 0) for fp8, NULL for bf16.
  * ctx_len  [B] int32 (device).
  * scores   [B,T,ld_scores] fp32 output; columns 0..Lmax-1 are written.
- * Supported: D in {64,128}, 1 <= H <= 64, ld_scores >= Lmax and a multiple
- * of 4.  Products are exact in fp32 and accumulate in fp32.
+ * Supported: D in {64,128}, 1 <= H <= 64, Lmax * D * element size < 2^31,
+ * ld_scores >= Lmax and a multiple of 4.  Products are exact in fp32 and
+ * accumulate in fp32.
  */
 dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t dtype, const float* q_scale,
                                 const float* w, const void* k, const float* k_scale,
