@@ -27,6 +27,9 @@ namespace {
 constexpr int kPfWaves = 8;    // queries per workgroup
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfTile = 128;   // keys per LDS tile
+constexpr int kParts = 4;      // independent fma chains of the head sum
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <bool FP8, int D, int HB>
 __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
@@ -89,21 +92,30 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     }
   }
 
-  const uint8_t* kb = k + (int64_t)b * Lmax * ROWB;
-  const float* ksb = FP8 ? k_scale + (int64_t)b * Lmax : nullptr;
+  // Keys, scales and scores through buffer resources over this sequence: a
+  // per-thread constant offset plus a scalar per-tile offset (no vector
+  // address arithmetic); reads past Lmax return zero, stores past it are
+  // dropped.
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k + (int64_t)b * Lmax * ROWB), 0, Lmax * ROWB, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(FP8 ? k_scale + (int64_t)b * Lmax : k_scale), 0, FP8 ? Lmax * 4 : 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t outr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, Lmax * 4, kBufferWord3);
   const int ntiles = (kc - k0 + kPfTile - 1) / kPfTile;
 
   i32x4 stage[CH];
   float stage_s = 1.f;
   auto gload = [&](int tile) {
-    const int base = k0 + tile * kPfTile;
+    const int base = __builtin_amdgcn_readfirstlane(k0 + tile * kPfTile);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int chunk = tid + c * kPfThreads;
-      const int key = min(base + chunk / CPR, Lmax - 1);
-      stage[c] = ld16(kb + (int64_t)key * ROWB + (chunk % CPR) * 16);
-    }
-    if (FP8 && tid < kPfTile) stage_s = ksb[min(base + tid, Lmax - 1)];
+    for (int c = 0; c < CH; ++c)
+      stage[c] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + c * kPfThreads) * 16,
+                                                       base * ROWB, 0));
+    if (FP8 && tid < kPfTile)
+      stage_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              sr, tid * 4, base * 4, 0));
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -153,17 +165,31 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
           }
         }
       }
-      float sc = 0.f;
+      // ReLU as a signed-integer max on the bit pattern (negative floats,
+      // -0 included, have negative patterns), head sum in kParts chains,
+      // the other 16 rows of each head block from lane l ^ 32.
+      float part[kParts];
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) part[p] = 0.f;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc = fmaf(wv[hb][r], fmaxf(acc[hb][r], 0.f), sc);
-      sc += __shfl_xor(sc, 32, kWave);
+        for (int r = 0; r < 16; ++r) {
+          const float x = __int_as_float(max(__float_as_int(acc[hb][r]), 0));
+          part[(hb * 16 + r) % kParts] = fmaf(wv[hb][r], x, part[(hb * 16 + r) % kParts]);
+        }
+      float sc = part[0];
+#pragma unroll
+      for (int p = 1; p < kParts; ++p) sc += part[p];
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc),
+                                                   false, false);
+        sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
       const int key = kbase + col;
       if (g == 0 && live && key < kc) {
-        float o = -INFINITY;
-        if (key <= pos) o = FP8 ? sc * kss[buf][sb * 32 + col] : sc;
-        srow[key] = o;
+        const float o = key <= pos ? (FP8 ? sc * kss[buf][sb * 32 + col] : sc) : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, col * 4, kbase * 4, 0);
       }
     }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
