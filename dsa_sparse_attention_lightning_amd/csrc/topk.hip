@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
     int Lmax, int k, int chunk, const uint32_t* __restrict__ hist_g,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_pos,
-    uint32_t* __restrict__ cand_cnt, int n_chunks) {
+    uint32_t* __restrict__ cand_cnt, int n_chunks, uint32_t* __restrict__ row_sel) {
   __shared__ uint32_t scan[kChWaves];
   __shared__ uint32_t sel[4];
   __shared__ uint32_t h[kBins1];
@@ -332,21 +332,31 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
   if (n <= k) return;
   const int c0 = blockIdx.x * chunk;
   const int c1 = min(n, c0 + chunk);
+  const float* src = scores + (int64_t)row * ld;
+  // the chunk's first batch of scores is requested before the histogram
+  uint32_t key[kPer / 4][4];
+  bool ok[kPer / 4][4];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) load4(src, c0 + kPer * tid + 4 * v, c1, key[v], ok[v]);
   const uint32_t* hg = hist_g + (int64_t)row * kBins1;
   for (int i = tid; i < kBins1; i += kChThreads) h[i] = hg[i];
   __syncthreads();
   select_bin<kBins1, kChThreads>(h, (uint32_t)k, scan, sel);
   const uint32_t b1 = sel[0];
-  const float* src = scores + (int64_t)row * ld;
+  if (blockIdx.x == 0 && tid == 0) {  // the row's selection, for the finishing pass
+    row_sel[3 * row] = b1;
+    row_sel[3 * row + 1] = sel[1];
+    row_sel[3 * row + 2] = sel[1] + h[b1];
+  }
   uint32_t* ck = cand_key + (int64_t)row * Lmax;
   int32_t* cp = cand_pos + (int64_t)row * Lmax;
   uint32_t run = 0;
   for (int base = c0; base < c1; base += kPer * kChThreads) {
     const int s0 = base + kPer * tid;
-    uint32_t key[kPer / 4][4];
-    bool ok[kPer / 4][4];
+    if (base != c0) {
 #pragma unroll
-    for (int v = 0; v < kPer / 4; ++v) load4(src, s0 + 4 * v, c1, key[v], ok[v]);
+      for (int v = 0; v < kPer / 4; ++v) load4(src, s0 + 4 * v, c1, key[v], ok[v]);
+    }
     uint32_t c = 0;
 #pragma unroll
     for (int v = 0; v < kPer / 4; ++v)
@@ -376,7 +386,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
     int Lmax, int k, int chunk, int n_chunks, uint32_t* __restrict__ hist_g,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
-    const uint32_t* __restrict__ cand_cnt, int32_t* __restrict__ idx) {
+    const uint32_t* __restrict__ cand_cnt, const uint32_t* __restrict__ row_sel,
+    int32_t* __restrict__ idx) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
   const int tid = threadIdx.x;
@@ -391,15 +402,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
     return;
   }
-  // the histogram and the slice counts are loaded together
+  // the row's selection (written by the collect pass) and the slice counts
   const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
-  for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = hg[i];
-  __syncthreads();
-  select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
-  const uint32_t b1 = sm.sel[0];
-  const uint32_t above1 = sm.sel[1];
-  const uint32_t listed = above1 + sm.hist[b1];
-  __syncthreads();
+  const uint32_t b1 = row_sel[3 * row];
+  const uint32_t above1 = row_sel[3 * row + 1];
+  const uint32_t listed = row_sel[3 * row + 2];
   for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;  // ready for the next call
   if (listed > (uint32_t)kTkCap) {
     finish_from_row(scores + (int64_t)row * ld, n, b1, above1, k, out, sm);
@@ -472,16 +479,21 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct TopkWs {
   uint32_t* hist;
+  uint32_t* sel;
   uint32_t* cnt;
   uint32_t* key;
   int32_t* pos;
 };
 
+// Workspace: per-row histograms (kept zero between calls), per-row selection
+// {b1, count above b1, listed}, per-chunk counts, candidate keys and positions.
 TopkWs carve(void* ws, int rows, int Lmax, int n_chunks) {
   unsigned char* p = reinterpret_cast<unsigned char*>(ws);
   TopkWs w;
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins1 * 4);
+  w.sel = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 3 * 4);
   w.cnt = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * n_chunks * 4);
   w.key = reinterpret_cast<uint32_t*>(p);
@@ -500,7 +512,7 @@ size_t topk_workspace_bytes(int B, int T, int Lmax, int) {
   const TopkPlan p = plan_topk(B, T, Lmax);
   if (!p.chunked) return 0;
   const size_t rows = (size_t)B * T;
-  return align256(rows * kBins1 * 4) + align256(rows * p.n_chunks * 4) +
+  return align256(rows * kBins1 * 4) + align256(rows * 3 * 4) + align256(rows * p.n_chunks * 4) +
          align256(rows * Lmax * 4) + align256(rows * Lmax * 4);
 }
 
@@ -529,11 +541,13 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
     hipLaunchKernelGGL(topk_chunk_hist_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
                        ctx_len, T, Lmax, k, p.chunk, w.hist);
   hipLaunchKernelGGL(topk_chunk_collect_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
-                     ctx_len, T, Lmax, k, p.chunk, w.hist, w.key, w.pos, w.cnt, p.n_chunks);
+                     ctx_len, T, Lmax, k, p.chunk, w.hist, w.key, w.pos, w.cnt, p.n_chunks,
+                     w.sel);
   hipError_t e = set_smem_attr((const void*)topk_finish_kernel, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kTkThreads), smem, stream, scores, ld,
-                     ctx_len, T, Lmax, k, p.chunk, p.n_chunks, w.hist, w.key, w.pos, w.cnt, idx);
+                     ctx_len, T, Lmax, k, p.chunk, p.n_chunks, w.hist, w.key, w.pos, w.cnt,
+                     w.sel, idx);
   return hipGetLastError();
 }
 
