@@ -139,3 +139,58 @@ def test_kv_append_rejects_bad_arguments(lib):
     assert f(16, 16, None, 1, 1, 64, 576, 128, 1, 16, 16, 16, None) == 1        # no ctx_len
     assert f(16, 16, 16, 1, 1, 64, 576, 128, 1, 16, 18, 16, None) == 1          # misaligned
     assert "aligned" in _err(lib)
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "dsa_indexcache.h"
+
+int main(void) {
+  /* a validation error comes back as a status and a message, nothing launched */
+  if (dsa_topk(NULL, 4096, NULL, 1, 1, 4096, 8, NULL, NULL, 0, NULL) != DSA_ERR_INVALID_ARG)
+    return 1;
+  if (strstr(dsa_last_error(), "NULL") == NULL) return 2;
+  /* host-only pattern search on a 4-layer cost matrix */
+  double c[16] = {0};
+  c[1 * 4 + 0] = 0.5;
+  c[2 * 4 + 0] = 0.9; c[2 * 4 + 1] = 0.1;
+  c[3 * 4 + 0] = 0.8; c[3 * 4 + 1] = 0.7; c[3 * 4 + 2] = 0.2;
+  char pats[3 * 5];
+  double tot[3];
+  if (indexcache_greedy_search(c, 4, 3, pats, tot) != DSA_OK) return 3;
+  double one = 0.0;
+  if (indexcache_pattern_cost(c, 4, "FFSS", &one) != DSA_OK) return 4;
+  dsa_stack_shape_t shape = {1, 1, 64, 128, 4096, 2048, 128, 576, 512, DSA_FP8_E4M3, 0.07f};
+  size_t need = 0;
+  if (indexcache_stack_workspace_size(&shape, &need) != DSA_OK) return 5;
+  printf("%s %s %s %.3f %.3f %zu\n", pats, pats + 5, pats + 10, tot[2], one, need);
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(lib, tmp_path):
+    """The C ABI header compiles as C99 with warnings as errors, and a C program
+    linked against the library gets statuses, messages and host-only search
+    results through it (no GPU work)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or ROCm headers not available")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o",
+           str(exe), "-L", libdir, "-ldsa_indexcache", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    words = r.stdout.split()
+    assert words[:3] == ["FFSF", "FFSS", "FSSS"]
+    assert abs(float(words[3]) - 2.2) < 1e-9 and abs(float(words[4]) - 0.8) < 1e-9
+    assert int(words[5]) > 0
