@@ -10,7 +10,8 @@ on every layer.  Inputs are seeded synthetic tensors resident in HBM before
 the timed region.
 
 Also reported on the same line:
-  * the same stack with all-F and with 'FSSS' x 12;
+  * the same stack with all-F and with 'FSSS' x 12, and the configured stack
+    captured into one HIP graph and replayed;
   * indexer + top-k time per layer and per 4-layer group (Hq = 0 stacks);
   * per-kernel average durations from HIP events on the launch stream, and the
     roofline of the dominant kernel;
@@ -171,6 +172,19 @@ def decode_bench(args, dev):
         log(f"{name:7s} {ms:8.3f} ms/step  {s.B / (ms * 1e-3):9.0f} tok/s  "
             f"indexer+topk {ms_i * 1e3 / s.n_layers:7.2f} us/layer  F={stats['n_indexer_calls']}")
     cut = 1.0 - res["FSSS"]["indexer_topk_ms_per_step"] / res["all-F"]["indexer_topk_ms_per_step"]
+
+    # ---- the configured stack captured once into a HIP graph and replayed
+    # (same kernels and arguments; the step without host launch overhead)
+    st = dsa.Stack(s.pattern, layers, ctx, **shape_kw(s))
+    st.run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.run()
+    ms_g = event_time_ms(lambda i=0: graph.replay(), args.steps, args.warmup)
+    res["config"]["graph_replay_ms_per_step"] = ms_g
+    log(f"config   {ms_g:8.3f} ms/step as HIP-graph replays")
+    del graph, st
 
     # ---- per-kernel durations (events around back-to-back launches)
     f_layers = [l for l, c in enumerate(s.pattern) if c == "F"]
