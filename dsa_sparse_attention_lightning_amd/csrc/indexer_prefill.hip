@@ -31,8 +31,12 @@ constexpr int kParts = 4;      // independent fma chains of the head sum
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
 
+// fp8: at most 128 registers per lane so that two workgroups share a CU (four
+// waves per SIMD hide each other's MFMA and epilogue; measured 3% faster than
+// two waves even with a few spilled registers).  bf16 needs more registers
+// (its query block is twice the size) and keeps two waves per SIMD.
 template <bool FP8, int D, int HB>
-__global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
+__global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
