@@ -77,15 +77,60 @@ __device__ void select_bin(const uint32_t* hist, uint32_t kk, uint32_t* scan, ui
   __syncthreads();
 }
 
-__device__ __forceinline__ void load4(const float* src, int s, int n, uint32_t (&key)[4],
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Score loads go through a buffer resource over the first n scores of a row,
+// rounded up to whole 16-byte vectors (rows are padded to a multiple of 4
+// floats): a load is never partly in range, loads past the end read zero,
+// and no branch separates issuing a batch of loads from using it, so a
+// thread's loads are all in flight together.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* src, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, ((n + 3) & ~3) * 4, kBufferWord3);
+}
+
+// Scores s..s+3 (s a multiple of 4) as keys; ok marks those below n.
+__device__ __forceinline__ void load4(__amdgpu_buffer_rsrc_t r, int s, int n, uint32_t (&key)[4],
                                       bool (&ok)[4]) {
-  if (s < n) {
-    const float4 v = *reinterpret_cast<const float4*>(src + s);
-    key[0] = float_key(v.x); key[1] = float_key(v.y);
-    key[2] = float_key(v.z); key[3] = float_key(v.w);
-  }
+  const float4 v =
+      __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, s * 4, 0, 0));
+  key[0] = float_key(v.x); key[1] = float_key(v.y);
+  key[2] = float_key(v.z); key[3] = float_key(v.w);
 #pragma unroll
   for (int j = 0; j < 4; ++j) ok[j] = (s + j) < n;
+}
+
+// Unordered pass over the n visible scores of a row by a whole kTkThreads
+// workgroup: f(key) for each, with kRowBatch 16-byte loads per thread in
+// flight (vector v of a batch is at 4 * (tid + kTkThreads * v)).
+constexpr int kRowBatch = 4;
+template <typename F>
+__device__ __forceinline__ void for_each_key(__amdgpu_buffer_rsrc_t r, int n, F f) {
+  for (int base = 0; base < n; base += 4 * kTkThreads * kRowBatch) {
+    uint32_t key[kRowBatch][4];
+    bool ok[kRowBatch][4];
+#pragma unroll
+    for (int v = 0; v < kRowBatch; ++v)
+      load4(r, base + 4 * ((int)threadIdx.x + kTkThreads * v), n, key[v], ok[v]);
+#pragma unroll
+    for (int v = 0; v < kRowBatch; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ok[v][j]) f(key[v][j]);
+  }
+}
+
+// Copy a 4096-bin histogram from global memory into LDS with 16-byte loads,
+// all of a thread's loads issued before the first LDS write.
+template <int NTH>
+__device__ __forceinline__ void hist_to_lds(const uint32_t* __restrict__ g, uint32_t* l) {
+  constexpr int V = kBins1 / (4 * NTH);
+  static_assert(V * 4 * NTH == kBins1, "whole vectors per thread");
+  i32x4 v[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) v[u] = ld16(g + 4 * (threadIdx.x + NTH * u));
+#pragma unroll
+  for (int u = 0; u < V; ++u) *reinterpret_cast<i32x4*>(l + 4 * (threadIdx.x + NTH * u)) = v[u];
 }
 
 // Ordered emission of the selected elements: key > tau, or key == tau and
@@ -172,16 +217,12 @@ __device__ void finish_from_list(int M, uint32_t b1, uint32_t above1, int k, int
 __device__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t above1, int k,
                                 int32_t* out, TopkSmem& sm) {
   const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t r = row_rsrc(src, n);
   for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
-  for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
-    uint32_t key[4];
-    bool ok[4];
-    load4(src, s, n, key, ok);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j] && (key[j] >> 20) == b1) atomicAdd(&sm.hist[(key[j] >> 10) & 1023u], 1u);
-  }
+  for_each_key(r, n, [&](uint32_t key) {
+    if ((key >> 20) == b1) atomicAdd(&sm.hist[(key >> 10) & 1023u], 1u);
+  });
   __syncthreads();
   select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1, sm.scan, sm.sel);
   const uint32_t b2 = sm.sel[0];
@@ -190,14 +231,9 @@ __device__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t a
   const uint32_t pre2 = (b1 << 10) | b2;
   for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
-  for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
-    uint32_t key[4];
-    bool ok[4];
-    load4(src, s, n, key, ok);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j] && (key[j] >> 10) == pre2) atomicAdd(&sm.hist[key[j] & 1023u], 1u);
-  }
+  for_each_key(r, n, [&](uint32_t key) {
+    if ((key >> 10) == pre2) atomicAdd(&sm.hist[key & 1023u], 1u);
+  });
   __syncthreads();
   select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1 - above2, sm.scan, sm.sel);
   const uint32_t b3 = sm.sel[0];
@@ -207,7 +243,7 @@ __device__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t a
   const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
   emit_selected(n, tau, take_eq, out, sm,
                 [&](int s, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
-                  load4(src, s, n, key, ok);
+                  load4(r, s, n, key, ok);
 #pragma unroll
                   for (int j = 0; j < 4; ++j) p[j] = s + j;
                 });
@@ -235,16 +271,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     return;
   }
   const float* src = scores + (int64_t)row * ld;
+  const __amdgpu_buffer_rsrc_t r = row_rsrc(src, n);
   for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
-  for (int s = 4 * tid; s < n; s += 4 * kTkThreads) {
-    uint32_t key[4];
-    bool ok[4];
-    load4(src, s, n, key, ok);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j]) atomicAdd(&sm.hist[key[j] >> 20], 1u);
-  }
+  for_each_key(r, n, [&](uint32_t key) { atomicAdd(&sm.hist[key >> 20], 1u); });
   __syncthreads();
   select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
   const uint32_t b1 = sm.sel[0];
@@ -255,28 +285,45 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     finish_from_row(src, n, b1, above1, k, out, sm);
     return;
   }
+  // Ordered copy of the candidates: a thread owns kPer consecutive scores of
+  // each batch, and the next batch is in flight while this one is copied.
+  constexpr int kBatch = kPer * kTkThreads;
+  uint32_t key[kPer / 4][4], nkey[kPer / 4][4];
+  bool ok[kPer / 4][4], nok[kPer / 4][4];
+#pragma unroll
+  for (int v = 0; v < kPer / 4; ++v) load4(r, kPer * tid + 4 * v, n, key[v], ok[v]);
   uint32_t run = 0;
-  for (int base = 0; base < n; base += 4 * kTkThreads) {
-    const int s = base + 4 * tid;
-    uint32_t key[4] = {0, 0, 0, 0};
-    bool ok[4];
-    load4(src, s, n, key, ok);
+  for (int base = 0; base < n; base += kBatch) {
+    const int s0 = base + kPer * tid;
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v) load4(r, s0 + kBatch + 4 * v, n, nkey[v], nok[v]);
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ok[j] = ok[j] && (key[j] >> 20) >= b1;
-      c += ok[j];
-    }
+    for (int v = 0; v < kPer / 4; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[v][j] = ok[v][j] && (key[v][j] >> 20) >= b1;
+        c += ok[v][j];
+      }
     uint32_t tot;
     uint32_t at = run + block_excl_scan<kTkWaves>(c, sm.scan, tot);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j]) {
-        sm.list_key[at] = key[j];
-        sm.list_pos[at] = s + j;
-        ++at;
-      }
+    for (int v = 0; v < kPer / 4; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ok[v][j]) {
+          sm.list_key[at] = key[v][j];
+          sm.list_pos[at] = s0 + 4 * v + j;
+          ++at;
+        }
     run += tot;
+#pragma unroll
+    for (int v = 0; v < kPer / 4; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        key[v][j] = nkey[v][j];
+        ok[v][j] = nok[v][j];
+      }
   }
   finish_from_list((int)listed, b1, above1, k, out, sm);
 }
@@ -286,7 +333,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
 __global__ __launch_bounds__(kChThreads) void topk_chunk_hist_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
     int Lmax, int k, int chunk, uint32_t* __restrict__ hist_g) {
-  __shared__ uint32_t h[kBins1];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kBins1];
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int n = visible(ctx_len, row, T, Lmax);
@@ -296,14 +343,14 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_hist_kernel(
   if (c0 >= c1) return;
   for (int i = tid; i < kBins1; i += kChThreads) h[i] = 0;
   __syncthreads();
-  const float* src = scores + (int64_t)row * ld;
+  const __amdgpu_buffer_rsrc_t r = row_rsrc(scores + (int64_t)row * ld, c1);
   // a thread owns kPer consecutive scores of each batch; all loads first
   for (int base = c0; base < c1; base += kPer * kChThreads) {
     const int s0 = base + kPer * tid;
     uint32_t key[kPer / 4][4];
     bool ok[kPer / 4][4];
 #pragma unroll
-    for (int v = 0; v < kPer / 4; ++v) load4(src, s0 + 4 * v, c1, key[v], ok[v]);
+    for (int v = 0; v < kPer / 4; ++v) load4(r, s0 + 4 * v, c1, key[v], ok[v]);
 #pragma unroll
     for (int v = 0; v < kPer / 4; ++v)
 #pragma unroll
@@ -325,21 +372,20 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
     uint32_t* __restrict__ cand_cnt, int n_chunks, uint32_t* __restrict__ row_sel) {
   __shared__ uint32_t scan[kChWaves];
   __shared__ uint32_t sel[4];
-  __shared__ uint32_t h[kBins1];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kBins1];
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int n = visible(ctx_len, row, T, Lmax);
   if (n <= k) return;
   const int c0 = blockIdx.x * chunk;
   const int c1 = min(n, c0 + chunk);
-  const float* src = scores + (int64_t)row * ld;
+  const __amdgpu_buffer_rsrc_t r = row_rsrc(scores + (int64_t)row * ld, c1);
   // the chunk's first batch of scores is requested before the histogram
   uint32_t key[kPer / 4][4];
   bool ok[kPer / 4][4];
 #pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) load4(src, c0 + kPer * tid + 4 * v, c1, key[v], ok[v]);
-  const uint32_t* hg = hist_g + (int64_t)row * kBins1;
-  for (int i = tid; i < kBins1; i += kChThreads) h[i] = hg[i];
+  for (int v = 0; v < kPer / 4; ++v) load4(r, c0 + kPer * tid + 4 * v, c1, key[v], ok[v]);
+  hist_to_lds<kChThreads>(hist_g + (int64_t)row * kBins1, h);
   __syncthreads();
   select_bin<kBins1, kChThreads>(h, (uint32_t)k, scan, sel);
   const uint32_t b1 = sel[0];
@@ -355,7 +401,7 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
     const int s0 = base + kPer * tid;
     if (base != c0) {
 #pragma unroll
-      for (int v = 0; v < kPer / 4; ++v) load4(src, s0 + 4 * v, c1, key[v], ok[v]);
+      for (int v = 0; v < kPer / 4; ++v) load4(r, s0 + 4 * v, c1, key[v], ok[v]);
     }
     uint32_t c = 0;
 #pragma unroll
