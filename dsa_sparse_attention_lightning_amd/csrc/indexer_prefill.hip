@@ -75,24 +75,35 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     for (int s = kc + lane; s < k1; s += kWave) srow[s] = -INFINITY;
   if (kc <= k0) return;  // uniform over the workgroup
 
-  // Query fragments and head weights (zero for padded heads / idle waves).
+  // Query fragments and head weights (zero for padded heads; an idle wave
+  // reads the last query row and stores nothing).
   i32x4 qv[HB][NV];
   float wv[HB][16];
+  {
+    // Buffer resources over this row's query block, weights and scales:
+    // the loads are unconditional (all in flight together) and a padded
+    // head (h >= H) reads zeros, so it adds nothing to any score.
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + row * H * ROWB), 0, H * ROWB, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(w + row * H), 0, H * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t qsr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(FP8 ? q_scale + row * H : w), 0, FP8 ? H * 4 : 0, kBufferWord3);
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int head = hb * 32 + col;
-    const uint8_t* qp = q + (row * H + head) * ROWB + g * HALF;
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = hb * 32 + col;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) qv[hb][v] = (head < H) ? ld16(qp + 16 * v) : i32x4{0, 0, 0, 0};
+      for (int v = 0; v < NV; ++v)
+        qv[hb][v] = __builtin_bit_cast(
+            i32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, head * ROWB + g * HALF + 16 * v, 0, 0));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      float wt = 0.f;
-      if (h < H && live) {
-        wt = w[row * H + h];
-        if (FP8) wt *= q_scale[row * H + h];
+      for (int r = 0; r < 16; ++r) {
+        const int h = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float wt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, h * 4, 0, 0));
+        if (FP8)
+          wt *= __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qsr, h * 4, 0, 0));
+        wv[hb][r] = wt;
       }
-      wv[hb][r] = wt;
     }
   }
 
