@@ -50,7 +50,12 @@ constexpr int kPitch = kPitchChunks * 16; // 1184
 constexpr int kTileLoads = kRows * kPitchChunks / kWave;  // 37 wave-loads per tile
 static_assert(kRows * kPitchChunks == kTileLoads * kWave, "a tile is whole wave-loads");
 constexpr int kTileBytes = kRows * kPitch;                // 37888
-constexpr int kMaxSplitRows = 1024;
+// Longest slice a workgroup takes (its row list and score bias live in LDS;
+// each thread keeps its share of the list in registers while the first
+// gathers are issued, so fewer waves take shorter slices).  2048 rows let a
+// four-wave workgroup take a whole top-2048 set: no split-KV partials and no
+// combine when the rows alone fill the GPU (prefill).
+__host__ __device__ constexpr int max_split_rows(int nw) { return nw == 4 ? 2048 : 1024; }
 constexpr int kOutPitch = 1040;           // LDS pitch of a staged 512-dim bf16 output row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -172,6 +177,7 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
     __bf16* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups,
     int n_work, int per_xcd) {
   constexpr int NT = NW * kWave;
+  constexpr int kMaxSplitRows = max_split_rows(NW);
   constexpr int KJ = (kTileLoads + NW - 1) / NW;  // DMA instructions per wave per tile
   // Three tile buffers, as separate LDS objects so that the compiler can tell
   // that reading one buffer does not depend on the DMA still writing another.
@@ -564,7 +570,7 @@ SplitPlan plan_split(int B, int T, int Hq, int k) {
   // partials (the size of ~450 gathered rows), so keep splits long.
   int ns = (kAttnWgTarget + base - 1) / base;
   ns = min(ns, max(1, tiles / (kAttnMinSplitRows / kRows)));
-  ns = max(ns, (k + kMaxSplitRows - 1) / kMaxSplitRows);
+  ns = max(ns, (k + max_split_rows(p.nw) - 1) / max_split_rows(p.nw));
   ns = max(1, min(ns, tiles));
   const int tiles_per = (tiles + ns - 1) / ns;
   p.rows_per_split = tiles_per * kRows;

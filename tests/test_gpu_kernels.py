@@ -126,6 +126,8 @@ ATTN_CASES = [
     (3, 1, 32, 1000, [1000, 40, 1], 100, 7),       # padded rows, ragged tile
     (1, 3, 64, 600, [600], 200, 0),                 # prefill rows
     (4, 1, 128, 2048, [2048] * 4, 1000, 0),
+    (1, 256, 64, 4096, [4096], 2048, 5),            # one 2048-row slice per row
+    (1, 64, 128, 4096, [4096], 3000, 0),            # k above the slice cap: two slices
 ]
 
 
