@@ -453,6 +453,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   const uint32_t b1 = row_sel[3 * row];
   const uint32_t above1 = row_sel[3 * row + 1];
   const uint32_t listed = row_sel[3 * row + 2];
+  // Each slice is copied by its own group of tpc threads.  The first batch
+  // of every slice is requested now, before its length is known (slice c
+  // starts at c * chunk; entries past its length are ignored), so the copy
+  // does not wait for a second round trip.
+  const int tpc = kTkThreads / n_chunks;
+  const int cq = tid / tpc;  // this thread's slice (none when >= n_chunks)
+  const int sub = tid - cq * tpc;
+  const int64_t base = (int64_t)min(cq, n_chunks - 1) * chunk;
+  const int cap = (int)min((int64_t)chunk, (int64_t)Lmax - base);  // room of the slice
+  const uint32_t* ck = cand_key + (int64_t)row * Lmax + base;
+  const int32_t* cp = cand_pos + (int64_t)row * Lmax + base;
+  uint32_t kv[kGather];
+  int32_t pv[kGather];
+#pragma unroll
+  for (int u = 0; u < kGather; ++u) {
+    const int e = min(sub + u * tpc, cap - 1);
+    kv[u] = ck[e];
+    pv[u] = cp[e];
+  }
   for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;  // ready for the next call
   if (listed > (uint32_t)kTkCap) {
     finish_from_row(scores + (int64_t)row * ld, n, b1, above1, k, out, sm);
@@ -467,24 +486,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     if (tid == 0) sm.chunk_off[n_chunks] = tot;
   }
   __syncthreads();
-  const uint32_t* ck = cand_key + (int64_t)row * Lmax;
-  const int32_t* cp = cand_pos + (int64_t)row * Lmax;
-  const int tpc = kTkThreads / n_chunks;
-  const int c = tid / tpc;
-  if (c < n_chunks) {
-    const int sub = tid - c * tpc;
-    const uint32_t off = sm.chunk_off[c];
-    const int cn = (int)(sm.chunk_off[c + 1] - off);
-    const int64_t base = (int64_t)c * chunk;
-    // batches of kGather entries per thread, all loads issued first
-    for (int e0 = sub; e0 < cn; e0 += kGather * tpc) {
-      uint32_t kv[kGather];
-      int32_t pv[kGather];
+  if (cq < n_chunks) {
+    const uint32_t off = sm.chunk_off[cq];
+    const int cn = (int)(sm.chunk_off[cq + 1] - off);
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const int e = sub + u * tpc;
+      if (e < cn) {
+        sm.list_key[off + e] = kv[u];
+        sm.list_pos[off + e] = pv[u];
+      }
+    }
+    // the rest (long slices), batches of kGather entries per thread with
+    // all loads issued first
+    for (int e0 = sub + kGather * tpc; e0 < cn; e0 += kGather * tpc) {
 #pragma unroll
       for (int u = 0; u < kGather; ++u) {
         const int e = min(e0 + u * tpc, cn - 1);
-        kv[u] = ck[base + e];
-        pv[u] = cp[base + e];
+        kv[u] = ck[e];
+        pv[u] = cp[e];
       }
 #pragma unroll
       for (int u = 0; u < kGather; ++u) {

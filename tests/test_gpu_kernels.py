@@ -70,6 +70,20 @@ def _rand_scores(B, T, L, seed, kind="normal"):
         x = torch.where(m, torch.tensor(-0.0, device=DEV), torch.tensor(0.0, device=DEV))
     elif kind == "wide":
         x = torch.randn((B, T, L), generator=g, device=DEV) * 1e30
+    elif kind.startswith("cluster"):
+        # m scores in [1, 1.1) (one top-12-bit bin) over small noise, so the
+        # threshold bin holds m keys: "clusterM", or "clustertieM" with the
+        # cluster values on a grid of 101 (heavy ties inside the bin)
+        tie = kind.startswith("clustertie")
+        m = int(kind[len("clustertie" if tie else "cluster"):])
+        r = np.random.default_rng(seed)
+        x = r.standard_normal((B, T, L)) * 0.05
+        for b in range(B):
+            for t in range(T):
+                at = r.choice(L, m, replace=False)
+                v = r.integers(0, 101, m) / 1000.0 if tie else r.random(m) * 0.1
+                x[b, t, at] = 1.0 + v
+        x = torch.from_numpy(x.astype(np.float32)).to(DEV)
     else:
         raise ValueError(kind)
     ld = (L + 3) // 4 * 4          # rows padded to a multiple of 4 floats
@@ -92,6 +106,13 @@ TOPK_CASES = [
     (2, 1, 40000, [40000, 39000], 2048, "equal"),                # chunked rows, list overflow
     (3, 1, 196608, [196608, 100000, 16385], 2048, "normal"),     # chunked, ragged rows
     (32, 1, 32768, [32768] * 32, 2048, "normal"),                # chunked, many rows
+    # crowded threshold bin: refined by one wave (m <= 3072) or by the block
+    (2, 1, 40000, [40000, 39000], 2048, "cluster2500"),          # chunked rows
+    (2, 1, 40000, [40000, 39000], 2048, "clustertie3072"),
+    (2, 1, 40000, [40000, 39000], 2048, "cluster5000"),
+    (1, 4, 8192, [8192], 2048, "cluster3000"),                   # row kernel (T > 1)
+    (1, 4, 8192, [8192], 2048, "clustertie2200"),
+    (1, 4, 8192, [8192], 1000, "cluster6000"),
 ]
 
 
