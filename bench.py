@@ -533,6 +533,9 @@ def main():
                     help="run only the pattern-search leg and print its JSON object")
     ap.add_argument("--kv-append-only", action="store_true",
                     help="run only the KV-cache append leg and print its JSON object")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill legs (kernels and 4-layer stack) and print "
+                         "their JSON object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference for hardware traffic counters)")
@@ -563,6 +566,10 @@ def main():
         return
     if args.kv_append_only:
         print(json.dumps({"kv_append": kv_append_bench(dev)}), flush=True)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_bench(dev),
+                          "prefill_stack": prefill_stack_bench(dev)}), flush=True)
         return
     s, layers, res, cut, kernels, roof = decode_bench(args, dev)
     main_res = res["config"]
