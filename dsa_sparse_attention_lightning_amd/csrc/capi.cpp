@@ -57,10 +57,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kMaxTopk = 16384;
 constexpr int kMaxAttnK = 65536;
-constexpr int kMaxSearchK = 8192;
+constexpr int kMaxSearchK = 8192;  // one row's index list is staged in 32 KB of LDS
 // Kernels address one sequence's cache through a buffer resource with a
 // 32-bit byte range.
-constexpr int64_t kMaxSeqBytes = 2147483647LL;  // one row's index list is staged in 32 KB of LDS
+constexpr int64_t kMaxSeqBytes = 2147483647LL;
 
 dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
                            const float* q_scale, const float* w, const void* k,
@@ -127,6 +127,9 @@ dsa_status_t check_attn(const char* fn, const void* q, const void* kv, const int
         "%s: Hq must be a multiple of 16 in 16..1024 (got %d)", fn, Hq);
   CHECK(k >= 1 && k <= kMaxAttnK, DSA_ERR_UNSUPPORTED, "%s: k must be in 1..%d (got %d)", fn,
         kMaxAttnK, k);
+  CHECK((int64_t)Lmax * d_qk * 2 <= kMaxSeqBytes, DSA_ERR_UNSUPPORTED,
+        "%s: Lmax (%d) latent rows of %d bf16 exceed %lld bytes per sequence", fn, Lmax, d_qk,
+        (long long)kMaxSeqBytes);
   CHECK((int64_t)B * T <= 2147483647LL / 2, DSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
   CHECK(scale > 0.f && scale == scale, DSA_ERR_INVALID_ARG, "%s: scale must be > 0", fn);
   CHECK_PTR(q);

@@ -120,7 +120,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx
  * q [B,T,Hq,d_qk] bf16, kv [B,Lmax,d_qk] bf16, idx [B,T,k] int32,
  * out [B,T,Hq,d_v] bf16 (round to nearest even from fp32),
  * lse [B,T,Hq] fp32 or NULL.  Softmax and accumulation are fp32.
- * Supported: d_qk == 576, d_v == 512, Hq a multiple of 16, 1 <= k <= 65536.
+ * Supported: d_qk == 576, d_v == 512, Hq a multiple of 16 in 16..1024,
+ * 1 <= k <= 65536, Lmax * d_qk * 2 < 2^31 (one sequence's latent rows).
  * workspace: dsa_sparse_attn_workspace_size bytes (may be 0 / NULL when
  * 0): when the selected rows are split across workgroups it holds the
  * per-slice outputs (bf16, normalised by their own softmax sums) and their

@@ -92,6 +92,32 @@ def test_attn_rejects_unsupported(lib):
                  None) == _lib.DSA_ERR_WORKSPACE
 
 
+def test_limits_are_enforced_on_the_host(lib):
+    """Shapes past what the kernels address are rejected before any launch."""
+    f = lib.dsa_indexer_scores
+    # one sequence's bf16 keys above 2^31 bytes (buffer-resource range)
+    assert f(16, 0, None, 16, 16, None, 16, 1, 1, 64, 128, 1 << 23, 16, 1 << 23, None) == 2
+    assert "per sequence" in _err(lib) or "bytes" in _err(lib)
+    # B * T above 65535 indexer rows
+    assert f(16, 0, None, 16, 16, None, 16, 300, 300, 64, 128, 4096, 16, 4096, None) == 2
+    a = lib.dsa_sparse_attn
+    assert a(16, 16, 16, 16, 1, 1, 1040, 100, 8, 576, 512, 0.1, 16, None, None, 0, None) == 2
+    assert "Hq" in _err(lib)
+    assert a(16, 16, 16, 16, 1, 1, 128, 1 << 17, 65537, 576, 512, 0.1, 16, None, None, 0,
+             None) == 2
+    assert "k must be" in _err(lib)
+    # latent rows of one sequence above 2^31 bytes
+    assert a(16, 16, 16, 16, 1, 1, 128, 1 << 21, 2048, 576, 512, 0.1, 16, None, None, 0,
+             None) == 2
+    assert "per sequence" in _err(lib)
+    assert a(16, 16, 16, 16, 1, 9, 128, 8, 8, 576, 512, 0.1, 16, None, None, 0, None) == 1
+    assert "exceeds Lmax" in _err(lib)
+    need = ctypes.c_size_t()
+    assert lib.dsa_topk_workspace_size(1, 1, 4096, 16, None) == 1
+    assert lib.dsa_sparse_attn_workspace_size(1, 1, 100, 16, 512, ctypes.byref(need)) == 1
+    assert lib.indexcache_stack_workspace_size(None, ctypes.byref(need)) == 1
+
+
 def _stack_args(pattern, n):
     layers = (_lib.Layer * n)()
     for i in range(n):
