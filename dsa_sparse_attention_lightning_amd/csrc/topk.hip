@@ -66,13 +66,21 @@ __device__ void select_bin(const uint32_t* hist, uint32_t kk, uint32_t* scan, ui
   }
   uint32_t total;
   uint32_t above = block_excl_scan<NTH / kWave>(sum, scan, total);
+  // one bin of one thread holds the kk-th element: find it in registers and
+  // write once
+  int hit = -1;
+  uint32_t hit_above = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (above < kk && kk <= above + c[i]) {
-      sel[0] = NB - 1 - (tid * PER + i);
-      sel[1] = above;
+      hit = i;
+      hit_above = above;
     }
     above += c[i];
+  }
+  if (hit >= 0) {
+    sel[0] = NB - 1 - (tid * PER + hit);
+    sel[1] = hit_above;
   }
   __syncthreads();
 }
