@@ -26,16 +26,17 @@
 // or w * q_scale (fp8: the positive per-row scales commute with the ReLU) and
 // sums the heads: 16 rows per lane in registers in four independent chains,
 // the other 16 in lane l ^ 32.  Lanes 0..31 then store 32 consecutive fp32
-// scores (times the key's scale for fp8) or -inf past pos.  The launch bound
-// of two workgroups per CU caps a wave at 256 registers, which keeps the MFMA
-// accumulators in VGPRs where the epilogue reads them.
+// scores (times the key's scale for fp8) or -inf past pos.  A workgroup is
+// eight waves, about one workgroup per CU (two waves per SIMD), and the launch
+// bound of two waves per SIMD caps a wave at 256 registers, which keeps the
+// MFMA accumulators in VGPRs where the epilogue reads them.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;  // two per SIMD at one workgroup per CU
 
 constexpr int kTileBytes = 8192;   // key bytes per wave step
 constexpr int kHistBits = 12;      // first radix digit of the top-k selection
@@ -233,8 +234,9 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   }
 }
 
-// Workgroups per launch the tile split aims for (one per CU measured best:
-// 512 and 1024 were 2-25% slower at the 128K decode shape).
+// Workgroups per launch the tile split aims for (one per CU measured best at
+// the 128K decode shape: with four-wave workgroups 512 and 1024 were 2-25%
+// slower; with eight-wave workgroups 128 was 12% slower).
 constexpr int kDecWgTarget = 256;
 
 template <int D, bool FP8, int HB>
