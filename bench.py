@@ -186,6 +186,21 @@ def decode_bench(args, dev):
     log(f"config   {ms_g:8.3f} ms/step as HIP-graph replays")
     del graph, st
 
+    # ---- the same stack with F layers through the fused indexer + top-k
+    # (scores kept on chip; opt-in: slower than the separate kernels at this
+    # batch, faster at larger ones)
+    st = dsa.Stack(s.pattern, layers, ctx, fused_topk=True, **shape_kw(s))
+    if st.fused:
+        ms_f, _ = time_stack(st, args.steps, args.warmup)
+        st_fi = dsa.Stack(s.pattern, layers, ctx, fused_topk=True, **shape_kw(s, attn=False))
+        ms_fi, _ = time_stack(st_fi, args.steps, args.warmup)
+        res["config"]["fused_topk_ms_per_step"] = ms_f
+        res["config"]["fused_topk_indexer_topk_us_per_layer"] = ms_fi * 1e3 / s.n_layers
+        log(f"config   {ms_f:8.3f} ms/step with the fused indexer + top-k "
+            f"({ms_fi * 1e3 / s.n_layers:.2f} us/layer without attention)")
+        del st_fi
+    del st
+
     # ---- per-kernel durations (events around back-to-back launches)
     f_layers = [l for l, c in enumerate(s.pattern) if c == "F"]
     score = torch.empty((s.B, s.T, dsa.ld_for(s.Lmax)), dtype=torch.float32, device=dev)

@@ -6,6 +6,7 @@ must be contiguous device tensors; work is enqueued on torch's current stream.
 
     indexer_scores(q, w, k, ctx_len, q_scale=None, k_scale=None) -> scores [B,T,Lmax]
     topk(scores, ctx_len, k)                                     -> idx [B,T,k] int32
+    indexer_topk(q, w, k, ctx_len, k_sel, q_scale, k_scale)      -> idx (decode; no scores)
     sparse_attn(q, kv, idx, ctx_len, scale)                      -> (out, lse)
     kv_append(ctx_len, kv_new, kv_cache, k_new, k_cache, k_scale) -> None (caches in place)
     run_stack(pattern, layers, ...)                              -> stats dict
@@ -20,7 +21,8 @@ from typing import Dict, List, Optional, Sequence
 from . import _lib
 from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
 
-__all__ = ["indexer_scores", "topk", "topk_workspace_size", "sparse_attn",
+__all__ = ["indexer_scores", "topk", "topk_workspace_size", "indexer_topk",
+           "indexer_topk_workspace_size", "sparse_attn",
            "sparse_attn_workspace_size", "kv_append", "run_stack",
            "reuse_costs", "reuse_costs_workspace_size", "pattern_cost", "greedy_search",
            "Stack", "DSAError", "library", "ld_for"]
@@ -117,6 +119,46 @@ def topk(scores, ctx_len, k: int, out=None, workspace=None, stream=None):
         max(need.value, 1), dtype=torch.uint8, device=scores.device)
     _lib.check(lib.dsa_topk(_ptr(scores), ld, _ptr(ctx_len), B, T, Lmax, k, _ptr(out),
                             _ptr(ws), need.value, _stream(stream)))
+    return out
+
+
+def indexer_topk_workspace_size(B: int, T: int, H: int, D: int, Lmax: int, k: int,
+                                idx_dtype: str = "bf16") -> int:
+    """Workspace bytes of indexer_topk; raises DSAError for shapes it does not take."""
+    need = ctypes.c_size_t(0)
+    dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
+    _lib.check(library().dsa_indexer_topk_workspace_size(B, T, H, D, dt, Lmax, k,
+                                                         ctypes.byref(need)))
+    return need.value
+
+
+def indexer_topk(q, w, k_cache, ctx_len, k: int, q_scale=None, k_scale=None, out=None,
+                 workspace=None, stream=None):
+    """Indexer scores and top-k in one pass for decode shapes: [B,T,k] int32.
+
+    The same set as topk(indexer_scores(q, w, k_cache, ...), ctx_len, k), with
+    the scores kept on chip.  A reused `workspace` (uint8 device tensor of
+    indexer_topk_workspace_size bytes) must start zero-filled; calls leave the
+    part that must start at zero as they found it."""
+    torch = _torch()
+    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), 4)
+    _need(k_cache, "k_cache", (q.dtype,), 3)
+    _need(w, "w", (torch.float32,), 3)
+    _need(ctx_len, "ctx_len", (torch.int32,), 1)
+    B, T, H, D = q.shape
+    Lmax = k_cache.shape[1]
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=q.device)
+    _need(out, "out", (torch.int32,), 3)
+    lib = library()
+    dt = _idx_dtype(q)
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.dsa_indexer_topk_workspace_size(B, T, H, D, dt, Lmax, k, ctypes.byref(need)))
+    ws = workspace if workspace is not None else torch.zeros(need.value, dtype=torch.uint8,
+                                                             device=q.device)
+    _lib.check(lib.dsa_indexer_topk(_ptr(q), dt, _ptr(q_scale), _ptr(w), _ptr(k_cache),
+                                    _ptr(k_scale), _ptr(ctx_len), B, T, H, D, Lmax, k, _ptr(out),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -286,23 +328,38 @@ def greedy_search(cost, n_shared: int):
     return [(raw[m * (n + 1): m * (n + 1) + n].decode(), totals[m]) for m in range(n_shared)]
 
 
+def _fused_applies(B, T, H, D, Lmax, k, idx_dtype) -> bool:
+    try:
+        indexer_topk_workspace_size(B, T, H, D, Lmax, k, idx_dtype)
+        return True
+    except DSAError:
+        return False
+
+
 class Stack:
     """Pre-marshalled arguments of indexcache_run_stack for repeated calls."""
 
     def __init__(self, pattern: str, layers: Sequence[Dict], ctx_len, *, B, T, H, D, Lmax, k,
-                 Hq=0, idx_dtype="bf16", scale=1.0, d_qk=576, d_v=512, device=None):
+                 Hq=0, idx_dtype="bf16", scale=1.0, d_qk=576, d_v=512, device=None,
+                 fused_topk=False):
+        """fused_topk: F layers run indexer_topk (scores kept on chip) where
+        it takes the shape, instead of scores through score_buf + topk."""
         torch = _torch()
         self.pattern = pattern.encode()
         self.n_layers = len(layers)
         self._keep = [layers, ctx_len]
         self.layers = _layer_array(layers)
         dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
-        self.shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale))
+        flags = _lib.DSA_STACK_FUSED_TOPK if fused_topk else 0
+        self.shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale), flags)
         self.ctx_len = ctx_len
         dev = device if device is not None else ctx_len.device
         self.ld = ld_for(Lmax)
         self.idx_buf = torch.empty((B, T, k), dtype=torch.int32, device=dev)
-        self.score_buf = torch.empty((B, T, self.ld), dtype=torch.float32, device=dev)
+        self.fused = fused_topk and _fused_applies(B, T, H, D, Lmax, k, idx_dtype)
+        # the fused path never writes scores, so it needs no score buffer
+        self.score_buf = None if self.fused else torch.empty((B, T, self.ld),
+                                                             dtype=torch.float32, device=dev)
         need = ctypes.c_size_t(0)
         _lib.check(library().indexcache_stack_workspace_size(ctypes.byref(self.shape),
                                                              ctypes.byref(need)))

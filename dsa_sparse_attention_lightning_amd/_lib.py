@@ -27,7 +27,9 @@ class Layer(ctypes.Structure):
 class StackShape(ctypes.Structure):
     _fields_ = [("B", c_int), ("T", c_int), ("H", c_int), ("D", c_int), ("Lmax", c_int),
                 ("k", c_int), ("Hq", c_int), ("d_qk", c_int), ("d_v", c_int),
-                ("idx_dtype", c_int), ("scale", c_f32)]
+                ("idx_dtype", c_int), ("scale", c_f32), ("flags", c_int)]
+
+DSA_STACK_FUSED_TOPK = 1
 
 
 class StackStats(ctypes.Structure):
@@ -42,6 +44,10 @@ SIGNATURES = {
     "dsa_topk_workspace_size": (c_int, [c_int, c_int, c_int, c_int, c_size_p]),
     "dsa_topk": (c_int, [c_vp, c_i64, c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp,
                          ctypes.c_size_t, c_vp]),
+    "dsa_indexer_topk_workspace_size": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                c_size_p]),
+    "dsa_indexer_topk": (c_int, [c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
+                                 c_int, c_int, c_int, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "dsa_sparse_attn_workspace_size": (c_int, [c_int, c_int, c_int, c_int, c_int, c_size_p]),
     "dsa_sparse_attn": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                 c_int, c_f32, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),

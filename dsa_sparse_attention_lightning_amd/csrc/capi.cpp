@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -65,7 +66,8 @@ constexpr int64_t kMaxSeqBytes = 2147483647LL;
 dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
                            const float* q_scale, const float* w, const void* k,
                            const float* k_scale, const int32_t* ctx_len, int B, int T, int H,
-                           int D, int Lmax, const float* scores, int64_t ld) {
+                           int D, int Lmax, const float* scores, int64_t ld,
+                           bool with_scores = true) {
   CHECK(dtype == DSA_BF16 || dtype == DSA_FP8_E4M3, DSA_ERR_INVALID_ARG, "%s: unknown dtype %d",
         fn, (int)dtype);
   CHECK(B >= 1 && T >= 1 && Lmax >= 1, DSA_ERR_INVALID_ARG,
@@ -78,14 +80,15 @@ dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
   CHECK((int64_t)Lmax * D * (dtype == DSA_BF16 ? 2 : 1) <= kMaxSeqBytes, DSA_ERR_UNSUPPORTED,
         "%s: one sequence's key cache (Lmax %d x D %d) exceeds %lld bytes", fn, Lmax, D,
         (long long)kMaxSeqBytes);
-  CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
-        "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
-        Lmax);
+  if (with_scores)
+    CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
+          "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
+          Lmax);
   CHECK_PTR(q);
   CHECK_PTR(w);
   CHECK_PTR(k);
   CHECK_PTR(ctx_len);
-  CHECK_PTR(scores);
+  if (with_scores) CHECK_PTR(scores);
   if (dtype == DSA_FP8_E4M3) {
     CHECK(q_scale != nullptr && k_scale != nullptr, DSA_ERR_INVALID_ARG,
           "%s: fp8 inputs need q_scale and k_scale", fn);
@@ -99,17 +102,20 @@ dsa_status_t check_indexer(const char* fn, const void* q, dsa_dtype_t dtype,
 }
 
 dsa_status_t check_topk(const char* fn, const float* scores, int64_t ld, const int32_t* ctx_len,
-                        int B, int T, int Lmax, int k, const int32_t* idx) {
+                        int B, int T, int Lmax, int k, const int32_t* idx,
+                        bool with_scores = true) {
   CHECK(B >= 1 && T >= 1 && Lmax >= 1, DSA_ERR_INVALID_ARG,
         "%s: need B, T, Lmax >= 1 (got %d, %d, %d)", fn, B, T, Lmax);
   CHECK(T <= Lmax, DSA_ERR_INVALID_ARG, "%s: T (%d) exceeds Lmax (%d)", fn, T, Lmax);
   CHECK(k >= 1, DSA_ERR_INVALID_ARG, "%s: k must be >= 1 (got %d)", fn, k);
   CHECK(k <= kMaxTopk, DSA_ERR_UNSUPPORTED, "%s: k (%d) above %d", fn, k, kMaxTopk);
   CHECK((int64_t)B * T <= 2147483647LL / 2, DSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
-  CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
-        "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
-        Lmax);
-  CHECK_PTR(scores);
+  if (with_scores) {
+    CHECK(ld >= Lmax && ld % 4 == 0, DSA_ERR_INVALID_ARG,
+          "%s: ld_scores (%lld) must be >= Lmax (%d) and a multiple of 4", fn, (long long)ld,
+          Lmax);
+    CHECK_PTR(scores);
+  }
   CHECK_PTR(ctx_len);
   CHECK_PTR(idx);
   return DSA_OK;
@@ -143,8 +149,28 @@ dsa_status_t check_attn(const char* fn, const void* q, const void* kv, const int
 
 // The stack's workspace holds the top-k region (which must stay zero between
 // calls) followed by the attention region.
+bool uses_prefill_indexer(int T, int H, int D) { return T > 1 && dsa::indexer_prefill_supported(H, D); }
+
+// The fused indexer + top-k applies: the decode indexer kernel runs for this
+// shape and its chunk plan fits the finishing kernel.
+bool fused_topk_applies(int B, int T, int H, int D, dsa_dtype_t dtype, int Lmax, int k) {
+  return !uses_prefill_indexer(T, H, D) &&
+         dsa::indexer_topk_plan_ok(B, T, D, dtype == DSA_FP8_E4M3, Lmax, k);
+}
+
+bool stack_fuses_topk(const dsa_stack_shape_t* s) {
+  return (s->flags & DSA_STACK_FUSED_TOPK) &&
+         fused_topk_applies(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k);
+}
+
+// Room for the separate top-k's workspace and for the fused path's (both
+// start with the same zero-kept histograms and arrival words).
 size_t topk_region(const dsa_stack_shape_t* s) {
-  const size_t b = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
+  size_t b = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
+  if (fused_topk_applies(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k))
+    b = std::max(b, dsa::indexer_topk_workspace_bytes(s->B, s->T, s->D,
+                                                      s->idx_dtype == DSA_FP8_E4M3, s->Lmax,
+                                                      s->k));
   return (b + 255) & ~size_t(255);
 }
 
@@ -209,8 +235,6 @@ dsa_status_t check_cost_matrix(const char* fn, const double* C, int n) {
   return DSA_OK;
 }
 
-bool uses_prefill_indexer(int T, int H, int D) { return T > 1 && dsa::indexer_prefill_supported(H, D); }
-
 // row_hist: optional per-row top-k histogram filled on the way (decode kernel
 // only; pass null otherwise).
 dsa_status_t run_indexer(const void* q, dsa_dtype_t dtype, const float* q_scale, const float* w,
@@ -269,6 +293,45 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx
   return hip_status(dsa::launch_topk(scores, ld_scores, ctx_len, B, T, Lmax, k, idx, workspace,
                                      workspace_bytes, false, stream),
                     "topk launch");
+}
+
+dsa_status_t dsa_indexer_topk_workspace_size(int B, int T, int H, int D, dsa_dtype_t dtype,
+                                             int Lmax, int k, size_t* bytes) {
+  const char* fn = "dsa_indexer_topk_workspace_size";
+  CHECK(bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  CHECK(B >= 1 && T >= 1 && Lmax >= 1 && k >= 1 && H >= 1 && (D == 64 || D == 128),
+        DSA_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  CHECK(dtype == DSA_BF16 || dtype == DSA_FP8_E4M3, DSA_ERR_INVALID_ARG, "%s: unknown dtype %d",
+        fn, (int)dtype);
+  CHECK(fused_topk_applies(B, T, H, D, dtype, Lmax, k), DSA_ERR_UNSUPPORTED,
+        "%s: no fused plan for B=%d T=%d H=%d D=%d Lmax=%d (prefill shapes and more than %d "
+        "chunks per row use dsa_indexer_scores + dsa_topk)",
+        fn, B, T, H, D, Lmax, dsa::kTopkMaxChunks);
+  *bytes = dsa::indexer_topk_workspace_bytes(B, T, D, dtype == DSA_FP8_E4M3, Lmax, k);
+  return ok();
+}
+
+dsa_status_t dsa_indexer_topk(const void* q, dsa_dtype_t dtype, const float* q_scale,
+                              const float* w, const void* k, const float* k_scale,
+                              const int32_t* ctx_len, int B, int T, int H, int D, int Lmax,
+                              int k_sel, int32_t* idx, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  const char* fn = "dsa_indexer_topk";
+  dsa_status_t st = check_indexer(fn, q, dtype, q_scale, w, k, k_scale, ctx_len, B, T, H, D,
+                                  Lmax, nullptr, 0, false);
+  if (st != DSA_OK) return st;
+  st = check_topk(fn, nullptr, 0, ctx_len, B, T, Lmax, k_sel, idx, false);
+  if (st != DSA_OK) return st;
+  size_t need = 0;
+  st = dsa_indexer_topk_workspace_size(B, T, H, D, dtype, Lmax, k_sel, &need);
+  if (st != DSA_OK) return st;
+  CHECK(workspace_bytes >= need, DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given",
+        fn, need, workspace_bytes);
+  CHECK_PTR(workspace);
+  return hip_status(dsa::launch_indexer_topk_decode(q, dtype == DSA_FP8_E4M3, q_scale, w, k,
+                                                    k_scale, ctx_len, B, T, H, D, Lmax, k_sel,
+                                                    idx, workspace, stream),
+                    "fused indexer + top-k launch");
 }
 
 dsa_status_t dsa_sparse_attn_workspace_size(int B, int T, int Hq, int k, int d_v,
@@ -373,6 +436,9 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
   }
   const dsa_stack_shape_t& s = *shape;
   CHECK(s.Hq >= 0, DSA_ERR_INVALID_ARG, "%s: Hq must be >= 0", fn);
+  CHECK((s.flags & ~DSA_STACK_FUSED_TOPK) == 0, DSA_ERR_INVALID_ARG, "%s: unknown flags 0x%x",
+        fn, (unsigned)s.flags);
+  const bool fused = stack_fuses_topk(shape);
   size_t need = 0;
   {
     dsa_status_t st = indexcache_stack_workspace_size(shape, &need);
@@ -388,9 +454,10 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
     if (pattern[l] == 'F') {
       dsa_status_t st = check_indexer(what, L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
                                       L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
-                                      score_buf, ld_scores);
+                                      score_buf, ld_scores, !fused);
       if (st != DSA_OK) return st;
-      st = check_topk(what, score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k, idx_buf);
+      st = check_topk(what, score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k, idx_buf,
+                      !fused);
       if (st != DSA_OK) return st;
     }
     if (s.Hq > 0) {
@@ -399,6 +466,7 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
       if (st != DSA_OK) return st;
     }
   }
+  if (fused) CHECK_PTR(workspace);
   const size_t tk_bytes = topk_region(shape);
   void* attn_ws = workspace ? static_cast<unsigned char*>(workspace) + tk_bytes : nullptr;
   dsa_stack_stats_t st_local = {0, 0, 0};
@@ -410,7 +478,16 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
                            : dsa::topk_row_hist(workspace, s.B, s.T, s.Lmax, s.k);
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer_t& L = layers[l];
-    if (pattern[l] == 'F') {  // Full layer: fresh index set into the cache
+    if (pattern[l] == 'F' && fused) {  // Full layer, scores kept on chip
+      dsa_status_t st = hip_status(
+          dsa::launch_indexer_topk_decode(L.q_idx, s.idx_dtype == DSA_FP8_E4M3, L.q_idx_scale,
+                                          L.w, L.k_idx, L.k_idx_scale, ctx_len, s.B, s.T, s.H,
+                                          s.D, s.Lmax, s.k, idx_buf, workspace, stream),
+          "fused indexer + top-k launch");
+      if (st != DSA_OK) return st;
+      st_local.n_indexer_calls++;
+      st_local.n_topk_calls++;
+    } else if (pattern[l] == 'F') {  // Full layer: fresh index set into the cache
       dsa_status_t st = run_indexer(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
                                     L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
                                     score_buf, ld_scores, row_hist, stream);

@@ -101,4 +101,41 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   return before + incl - v;
 }
 
+// ---------------------------------------------------------------- radix select
+// Find the bin holding the kk-th largest element of a histogram of NB bins in
+// LDS (bins scanned from the top): writes {bin, count strictly above it} to
+// sel[0..1] in LDS.  `scan` holds NTH / 64 words.  All NTH threads call it;
+// it ends with a barrier.
+template <int NB, int NTH>
+__device__ void select_bin(const uint32_t* hist, uint32_t kk, uint32_t* scan, uint32_t* sel) {
+  constexpr int PER = NB / NTH;  // bins per thread
+  const int tid = threadIdx.x;
+  uint32_t c[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = hist[NB - 1 - (tid * PER + i)];
+    sum += c[i];
+  }
+  uint32_t total;
+  uint32_t above = block_excl_scan<NTH / kWave>(sum, scan, total);
+  // one bin of one thread holds the kk-th element: find it in registers and
+  // write once
+  int hit = -1;
+  uint32_t hit_above = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (above < kk && kk <= above + c[i]) {
+      hit = i;
+      hit_above = above;
+    }
+    above += c[i];
+  }
+  if (hit >= 0) {
+    sel[0] = NB - 1 - (tid * PER + hit);
+    sel[1] = hit_above;
+  }
+  __syncthreads();
+}
+
 }  // namespace dsa

@@ -22,9 +22,11 @@
 //     atomics into a per-row histogram), a second compacts each chunk's
 //     candidates in order into its own slice of a candidate buffer, and a
 //     per-row workgroup concatenates the slices and finishes 3-4.  The
-//     per-row histogram is cleared again by that last kernel, so the
-//     workspace holding it must be zero before the first call and is left
-//     zero by every call.
+//     per-row histogram (and the arrival word that the fused decode indexer
+//     meets at) is cleared again by that last kernel, so the workspace
+//     holding them must be zero before the first call and is left zero by
+//     every call.  The fused decode indexer produces the histogram and the
+//     slices itself and runs only the finishing kernel.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -38,7 +40,7 @@ constexpr int kBins1 = 4096;      // top 12 bits
 constexpr int kBins2 = 1024;      // next 10, last 10
 constexpr int kChThreads = 256;   // chunk workgroups
 constexpr int kChWaves = kChThreads / kWave;
-constexpr int kMaxChunks = 256;
+constexpr int kMaxChunks = kTopkMaxChunks;
 constexpr int kPer = 16;         // scores per thread per chunk batch (4096 per workgroup)
 constexpr int kGather = 8;       // candidate loads in flight per thread
 
@@ -50,40 +52,6 @@ struct TopkSmem {
   uint32_t sel[4];
   uint32_t chunk_off[kMaxChunks + 1];
 };
-
-// Find the bin holding the kk-th largest element (bins scanned from the top):
-// writes {bin, count strictly above it} to sel[0..1].  All NTH threads call.
-template <int NB, int NTH>
-__device__ void select_bin(const uint32_t* hist, uint32_t kk, uint32_t* scan, uint32_t* sel) {
-  constexpr int PER = NB / NTH;  // bins per thread
-  const int tid = threadIdx.x;
-  uint32_t c[PER];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = hist[NB - 1 - (tid * PER + i)];
-    sum += c[i];
-  }
-  uint32_t total;
-  uint32_t above = block_excl_scan<NTH / kWave>(sum, scan, total);
-  // one bin of one thread holds the kk-th element: find it in registers and
-  // write once
-  int hit = -1;
-  uint32_t hit_above = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (above < kk && kk <= above + c[i]) {
-      hit = i;
-      hit_above = above;
-    }
-    above += c[i];
-  }
-  if (hit >= 0) {
-    sel[0] = NB - 1 - (tid * PER + hit);
-    sel[1] = hit_above;
-  }
-  __syncthreads();
-}
 
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
@@ -254,6 +222,64 @@ __device__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t a
                   load4(r, s, n, key, ok);
 #pragma unroll
                   for (int j = 0; j < 4; ++j) p[j] = s + j;
+                });
+}
+
+// Steps 3-4 reading the candidate slices from memory (the list would not fit
+// in LDS and there is no score row to re-read: the fused indexer keeps its
+// scores on chip).  List entry e lives in the slice c with chunk_off[c] <= e <
+// chunk_off[c + 1], at c * chunk + e - chunk_off[c]; sm.chunk_off holds the
+// n_chunks + 1 slice offsets.  Slow (a binary search per entry) but only
+// reached by rows whose threshold bin holds more than kTkCap elements.
+__device__ void finish_from_slices(const uint32_t* ck, const int32_t* cp, int chunk,
+                                   int n_chunks, int M, uint32_t b1, uint32_t above1, int k,
+                                   int32_t* out, TopkSmem& sm) {
+  const int tid = threadIdx.x;
+  M = min(M, (int)sm.chunk_off[n_chunks]);  // never past the last slice (they agree)
+  auto at = [&](int e) -> int64_t {
+    int lo = 0, hi = n_chunks;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)sm.chunk_off[mid] <= e) lo = mid; else hi = mid;
+    }
+    return (int64_t)lo * chunk + (e - (int)sm.chunk_off[lo]);
+  };
+  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < M; e += kTkThreads) {
+    const uint32_t key = ck[at(e)];
+    if ((key >> 20) == b1) atomicAdd(&sm.hist[(key >> 10) & 1023u], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1, sm.scan, sm.sel);
+  const uint32_t b2 = sm.sel[0];
+  const uint32_t above2 = sm.sel[1];
+  __syncthreads();
+  const uint32_t pre2 = (b1 << 10) | b2;
+  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < M; e += kTkThreads) {
+    const uint32_t key = ck[at(e)];
+    if ((key >> 10) == pre2) atomicAdd(&sm.hist[key & 1023u], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1 - above2, sm.scan, sm.sel);
+  const uint32_t b3 = sm.sel[0];
+  const uint32_t above3 = sm.sel[1];
+  __syncthreads();
+  const uint32_t tau = (b1 << 20) | (b2 << 10) | b3;
+  const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
+  emit_selected(M, tau, take_eq, out, sm,
+                [&](int e, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    ok[j] = (e + j) < M;
+                    if (ok[j]) {
+                      const int64_t a = at(e + j);
+                      key[j] = ck[a];
+                      p[j] = cp[a];
+                    }
+                  }
                 });
 }
 
@@ -435,13 +461,17 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
   if (tid == 0) cand_cnt[(int64_t)row * n_chunks + blockIdx.x] = (c0 < c1) ? run : 0u;
 }
 
-// Steps 3-4 for one row from the chunk slices; clears the row's histogram.
+// Steps 3-4 for one row from the chunk slices; clears the row's histogram
+// and arrival word.  scores is null after the fused indexer (no score row in
+// memory): an overflowing list is then read from the slices.  A row whose
+// arrival word has its top bit set (the fused indexer's row barrier gave up
+// waiting) gets an empty selection (all -1).
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
     int Lmax, int k, int chunk, int n_chunks, uint32_t* __restrict__ hist_g,
-    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
-    const uint32_t* __restrict__ cand_cnt, const uint32_t* __restrict__ row_sel,
-    int32_t* __restrict__ idx) {
+    uint32_t* __restrict__ arrive, const uint32_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_pos, const uint32_t* __restrict__ cand_cnt,
+    const uint32_t* __restrict__ row_sel, int32_t* __restrict__ idx) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
   const int tid = threadIdx.x;
@@ -449,6 +479,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   const int n = visible(ctx_len, row, T, Lmax);
   int32_t* out = idx + (int64_t)row * k;
   uint32_t* hg = hist_g + (int64_t)row * kBins1;
+  const uint32_t arrived = arrive[row];
+  __syncthreads();  // every thread has read the word before it is cleared
+  if (tid == 0) arrive[row] = 0u;
+  if (arrived & 0x80000000u) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = -1;
+    for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
+    return;
+  }
   if (n <= k) {
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     // the chunk kernels touched nothing for this row, but a fused
@@ -481,10 +519,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     pv[u] = cp[e];
   }
   for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;  // ready for the next call
-  if (listed > (uint32_t)kTkCap) {
-    finish_from_row(scores + (int64_t)row * ld, n, b1, above1, k, out, sm);
-    return;
-  }
   // concatenate the chunk slices in chunk order: prefix sum of the slice
   // counts, then each slice is copied by its own group of tpc threads
   {
@@ -494,6 +528,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     if (tid == 0) sm.chunk_off[n_chunks] = tot;
   }
   __syncthreads();
+  if (listed > (uint32_t)kTkCap) {
+    if (scores != nullptr)
+      finish_from_row(scores + (int64_t)row * ld, n, b1, above1, k, out, sm);
+    else
+      finish_from_slices(cand_key + (int64_t)row * Lmax, cand_pos + (int64_t)row * Lmax, chunk,
+                         n_chunks, (int)listed, b1, above1, k, out, sm);
+    return;
+  }
   if (cq < n_chunks) {
     const uint32_t off = sm.chunk_off[cq];
     const int cn = (int)(sm.chunk_off[cq + 1] - off);
@@ -551,21 +593,18 @@ TopkPlan plan_topk(int B, int T, int Lmax) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-struct TopkWs {
-  uint32_t* hist;
-  uint32_t* sel;
-  uint32_t* cnt;
-  uint32_t* key;
-  int32_t* pos;
-};
+}  // namespace
 
-// Workspace: per-row histograms (kept zero between calls), per-row selection
-// {b1, count above b1, listed}, per-chunk counts, candidate keys and positions.
-TopkWs carve(void* ws, int rows, int Lmax, int n_chunks) {
+// Workspace of the chunked selection: per-row histograms and arrival words
+// (kept zero between calls), per-row selection {b1, count above b1, listed},
+// per-chunk counts, candidate keys and positions.
+TopkWs topk_chunk_ws(void* ws, int rows, int Lmax, int n_chunks) {
   unsigned char* p = reinterpret_cast<unsigned char*>(ws);
   TopkWs w;
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins1 * 4);
+  w.arrive = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 4);
   w.sel = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * 3 * 4);
   w.cnt = reinterpret_cast<uint32_t*>(p);
@@ -576,6 +615,14 @@ TopkWs carve(void* ws, int rows, int Lmax, int n_chunks) {
   return w;
 }
 
+size_t topk_chunk_ws_bytes(int rows, int Lmax, int n_chunks) {
+  return align256((size_t)rows * kBins1 * 4) + align256((size_t)rows * 4) +
+         align256((size_t)rows * 3 * 4) + align256((size_t)rows * n_chunks * 4) +
+         2 * align256((size_t)rows * Lmax * 4);
+}
+
+namespace {
+
 hipError_t set_smem_attr(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
@@ -585,15 +632,13 @@ hipError_t set_smem_attr(const void* fn, size_t bytes) {
 size_t topk_workspace_bytes(int B, int T, int Lmax, int) {
   const TopkPlan p = plan_topk(B, T, Lmax);
   if (!p.chunked) return 0;
-  const size_t rows = (size_t)B * T;
-  return align256(rows * kBins1 * 4) + align256(rows * 3 * 4) + align256(rows * p.n_chunks * 4) +
-         align256(rows * Lmax * 4) + align256(rows * Lmax * 4);
+  return topk_chunk_ws_bytes(B * T, Lmax, p.n_chunks);
 }
 
 uint32_t* topk_row_hist(void* workspace, int B, int T, int Lmax, int) {
   const TopkPlan p = plan_topk(B, T, Lmax);
   if (!p.chunked || workspace == nullptr) return nullptr;
-  return carve(workspace, B * T, Lmax, p.n_chunks).hist;
+  return topk_chunk_ws(workspace, B * T, Lmax, p.n_chunks).hist;
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, int B, int T,
@@ -609,7 +654,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
                        ctx_len, T, Lmax, k, idx);
     return hipGetLastError();
   }
-  const TopkWs w = carve(workspace, rows, Lmax, p.n_chunks);
+  const TopkWs w = topk_chunk_ws(workspace, rows, Lmax, p.n_chunks);
   const dim3 grid(p.n_chunks, rows);
   if (!hist_ready)
     hipLaunchKernelGGL(topk_chunk_hist_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
@@ -617,10 +662,20 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
   hipLaunchKernelGGL(topk_chunk_collect_kernel, grid, dim3(kChThreads), 0, stream, scores, ld,
                      ctx_len, T, Lmax, k, p.chunk, w.hist, w.key, w.pos, w.cnt, p.n_chunks,
                      w.sel);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_finish(scores, ld, ctx_len, B, T, Lmax, k, p.chunk, p.n_chunks, w, idx,
+                            stream);
+}
+
+hipError_t launch_topk_finish(const float* scores, int64_t ld, const int32_t* ctx_len, int B,
+                              int T, int Lmax, int k, int chunk, int n_chunks, const TopkWs& w,
+                              int32_t* idx, hipStream_t stream) {
+  const size_t smem = sizeof(TopkSmem);
   hipError_t e = set_smem_attr((const void*)topk_finish_kernel, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(rows), dim3(kTkThreads), smem, stream, scores, ld,
-                     ctx_len, T, Lmax, k, p.chunk, p.n_chunks, w.hist, w.key, w.pos, w.cnt,
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(B * T), dim3(kTkThreads), smem, stream, scores, ld,
+                     ctx_len, T, Lmax, k, chunk, n_chunks, w.hist, w.arrive, w.key, w.pos, w.cnt,
                      w.sel, idx);
   return hipGetLastError();
 }

@@ -98,12 +98,46 @@ dsa_status_t dsa_indexer_scores(const void* q, dsa_dtype_t dtype, const float* q
  * workspace: dsa_topk_workspace_size bytes (may be 0 / NULL when 0).  Few
  * long rows are split across workgroups that meet in a per-row histogram
  * kept in the workspace: the workspace must be zero-filled before its first
- * use, and every call leaves it zero-filled again.
+ * use, and every call leaves the part that must start at zero (its leading
+ * histograms) zero again.
  */
 dsa_status_t dsa_topk_workspace_size(int B, int T, int Lmax, int k, size_t* bytes);
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx_len, int B,
                       int T, int Lmax, int k, int32_t* idx, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Indexer scores and top-k in one pass for one-query-row (decode) shapes
+ * (technical summary §1: the indexer scores every previous token and keeps
+ * the k most relevant; the scores are consumed only by that selection).
+ * idx [B,T,k_sel] is exactly what dsa_indexer_scores followed by dsa_topk
+ * write for the same inputs (the same fp32 scores decide the same
+ * selection), but the scores never reach memory: each workgroup keeps its
+ * keys' scores in LDS, the workgroups of a row meet at a per-row barrier in
+ * the workspace (device-scope atomics only) and each compacts its own
+ * candidates, then one workgroup per row completes the selection.
+ * Arguments are those of dsa_indexer_scores and dsa_topk (k_sel is dsa_topk's
+ * k), with the same limits.
+ * Supported where the one-query-row indexer kernel runs (T == 1, or H / D
+ * that the prefill kernel does not take) and a row splits into at most 1024
+ * chunks of eight 8 KB key tiles (Lmax up to 524288 fp8 keys at D = 128);
+ * dsa_indexer_topk_workspace_size returns DSA_ERR_UNSUPPORTED otherwise.
+ * workspace: dsa_indexer_topk_workspace_size bytes (device), zero-filled
+ * before its first use; every call leaves its leading histograms and
+ * arrival words zero again.  Its layout starts like dsa_topk's, so one
+ * zero-filled buffer of the larger size serves both.  Calls sharing a
+ * workspace must not run concurrently.  The barrier needs one row's
+ * workgroups (at most one per CU) resident together; should that not happen
+ * within a bounded wait (another kernel holding the GPU), the row gets an
+ * all -1 selection instead of a hang.
+ */
+dsa_status_t dsa_indexer_topk_workspace_size(int B, int T, int H, int D, dsa_dtype_t dtype,
+                                             int Lmax, int k_sel, size_t* bytes);
+dsa_status_t dsa_indexer_topk(const void* q, dsa_dtype_t dtype, const float* q_scale,
+                              const float* w, const void* k, const float* k_scale,
+                              const int32_t* ctx_len, int B, int T, int H, int D, int Lmax,
+                              int k_sel, int32_t* idx, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * Sparse MLA attention over the selected latent rows (technical summary §1:
@@ -184,11 +218,15 @@ typedef struct dsa_layer {
   float* lse;                /* [B,T,Hq] or NULL */
 } dsa_layer_t;
 
+/* dsa_stack_shape_t.flags */
+#define DSA_STACK_FUSED_TOPK 1 /* F layers: dsa_indexer_topk where it applies */
+
 typedef struct dsa_stack_shape {
   int B, T, H, D, Lmax, k;
   int Hq, d_qk, d_v;       /* Hq == 0: indexer + top-k only, no attention */
   dsa_dtype_t idx_dtype;
   float scale;             /* softmax scale of the sparse attention       */
+  int flags;               /* 0 or DSA_STACK_FUSED_TOPK                   */
 } dsa_stack_shape_t;
 
 typedef struct dsa_stack_stats {
@@ -203,13 +241,17 @@ typedef struct dsa_stack_stats {
  * layer inherits from the nearest PRECEDING F layer, so a leading S has
  * nothing to inherit and is rejected).  For layer l:
  *   'F': scores = dsa_indexer_scores(layer l) into score_buf, then
- *        dsa_topk into idx_buf              (the index cache is written)
+ *        dsa_topk into idx_buf              (the index cache is written);
+ *        with DSA_STACK_FUSED_TOPK in flags and a shape dsa_indexer_topk
+ *        takes, dsa_indexer_topk into idx_buf instead (the same set;
+ *        score_buf is then neither written nor needed and may be NULL)
  *   'S': nothing                            (idx_buf is reused in place)
  *   then, if Hq > 0, dsa_sparse_attn(layer l, idx_buf).
  * idx_buf [B,T,k] int32 holds the last F layer's set when the call returns.
  * score_buf [B,T,ld_scores] fp32 scratch, workspace sized by
  * indexcache_stack_workspace_size; like the top-k workspace it must be
- * zero-filled before its first use and is left that way by every call.
+ * zero-filled before its first use, and every call leaves the part that
+ * must start at zero zero again.  Zero-initialise the shape (flags).
  * stats (host, may be NULL) receives the
  * number of kernels of each kind that were enqueued.
  */

@@ -187,7 +187,7 @@ int main(void) {
   if (indexcache_greedy_search(c, 4, 3, pats, tot) != DSA_OK) return 3;
   double one = 0.0;
   if (indexcache_pattern_cost(c, 4, "FFSS", &one) != DSA_OK) return 4;
-  dsa_stack_shape_t shape = {1, 1, 64, 128, 4096, 2048, 128, 576, 512, DSA_FP8_E4M3, 0.07f};
+  dsa_stack_shape_t shape = {1, 1, 64, 128, 4096, 2048, 128, 576, 512, DSA_FP8_E4M3, 0.07f, 0};
   size_t need = 0;
   if (indexcache_stack_workspace_size(&shape, &need) != DSA_OK) return 5;
   printf("%s %s %s %.3f %.3f %zu\n", pats, pats + 5, pats + 10, tot[2], one, need);
@@ -220,3 +220,38 @@ def test_header_is_plain_c_and_links(lib, tmp_path):
     assert words[:3] == ["FFSF", "FFSS", "FSSS"]
     assert abs(float(words[3]) - 2.2) < 1e-9 and abs(float(words[4]) - 0.8) < 1e-9
     assert int(words[5]) > 0
+
+
+def test_fused_indexer_topk_host_checks(lib):
+    """The fused indexer + top-k takes one-query-row shapes whose rows split
+    into at most 1024 chunks, sizes its workspace like the chunked top-k
+    (plus the larger chunk-count array), and rejects bad calls on the host."""
+    need = ctypes.c_size_t()
+    ws = lib.dsa_indexer_topk_workspace_size
+    assert ws(8, 1, 64, 128, _lib.DSA_FP8_E4M3, 131072, 2048, ctypes.byref(need)) == 0
+    rows, L, chunks = 8, 131072, 131072 // 64 // 8
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need.value == (a(rows * 4096 * 4) + a(rows * 4) + a(rows * 12) + a(rows * chunks * 4)
+                          + 2 * a(rows * L * 4))
+    # 524288 fp8 keys of D = 128 are 1024 chunks; one more tile is not taken
+    assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 524288, 2048, ctypes.byref(need)) == 0
+    assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 524288 + 64, 2048,
+              ctypes.byref(need)) == _lib.DSA_ERR_UNSUPPORTED
+    # several query rows per sequence run the prefill indexer: not fused
+    assert ws(1, 16, 64, 128, _lib.DSA_FP8_E4M3, 8192, 2048,
+              ctypes.byref(need)) == _lib.DSA_ERR_UNSUPPORTED
+    assert "prefill" in _err(lib)
+    f = lib.dsa_indexer_topk
+    # fp8 without scales; NULL output; workspace too small
+    assert f(16, _lib.DSA_FP8_E4M3, None, 16, 16, None, 16, 1, 1, 64, 128, 4096, 64, 16, 16,
+             1 << 30, None) == _lib.DSA_ERR_INVALID_ARG
+    assert f(16, _lib.DSA_BF16, None, 16, 16, None, 16, 1, 1, 64, 128, 4096, 64, None, 16,
+             1 << 30, None) == _lib.DSA_ERR_INVALID_ARG
+    assert f(16, _lib.DSA_BF16, None, 16, 16, None, 16, 1, 1, 64, 128, 4096, 64, 16, 16, 8,
+             None) == _lib.DSA_ERR_WORKSPACE
+    # a stack shape with unknown flags is refused
+    p, n, layers, shape = _stack_args("FSSS", 4)
+    shape.flags = 6
+    st = lib.indexcache_run_stack(p, n, layers, ctypes.byref(shape), 16, 16, 16, 4096, 16,
+                                  1 << 30, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and "flags" in _err(lib)

@@ -7,7 +7,8 @@ After every step: the caches equal the oracle's append bit for bit, every F
 layer's index set satisfies the top-k boundary rule against the oracle's fp64
 scores on those caches, the shared index buffer holds the last F layer's set,
 and every layer's attention output matches the oracle run over the index set
-the GPU used.
+the GPU used.  The loop runs with the separate indexer and top-k kernels
+and, for fp8 keys, also with the fused indexer + top-k.
 """
 import sys
 
@@ -36,8 +37,9 @@ def cache_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("idx_dtype,D", [("fp8", 128), ("bf16", 64)])
-def test_append_then_stack_for_three_steps(idx_dtype, D):
+@pytest.mark.parametrize("idx_dtype,D,fused", [("fp8", 128, False), ("bf16", 64, False),
+                                               ("fp8", 128, True)])
+def test_append_then_stack_for_three_steps(idx_dtype, D, fused):
     B, Lmax, H, k, Hq = 2, 1200, 16, 128, 32
     pattern = "FSSF"
     ctx = [900, 517]
@@ -84,7 +86,8 @@ def test_append_then_stack_for_three_steps(idx_dtype, D):
             q, _ = gen.make_mla_layer(sq, l, DEV)
             L.update(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w, q=q)
         st = dsa.Stack(pattern, layers, ctx_t, B=B, T=1, H=H, D=D, Lmax=Lmax, k=k, Hq=Hq,
-                       idx_dtype=idx_dtype, scale=s.scale)
+                       idx_dtype=idx_dtype, scale=s.scale, fused_topk=fused)
+        assert st.fused == fused
         stats = st.run()
         torch.cuda.synchronize()
         assert stats["n_indexer_calls"] == pattern.count("F")
