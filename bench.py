@@ -159,6 +159,7 @@ def decode_bench(args, dev):
     pats = {"config": s.pattern, "all-F": "F" * s.n_layers,
             "FSSS": gen.tile_pattern("FSSS", s.n_layers)}
     res = {}
+    res_fused = dsa.Stack(s.pattern, layers, ctx, **shape_kw(s, attn=False)).fused
     for name, p in pats.items():
         st = dsa.Stack(p, layers, ctx, **shape_kw(s))
         ms, stats = time_stack(st, args.steps, args.warmup)
@@ -186,20 +187,19 @@ def decode_bench(args, dev):
     log(f"config   {ms_g:8.3f} ms/step as HIP-graph replays")
     del graph, st
 
-    # ---- the same stack with F layers through the fused indexer + top-k
-    # (scores kept on chip; opt-in: slower than the separate kernels at this
-    # batch, faster at larger ones)
-    st = dsa.Stack(s.pattern, layers, ctx, fused_topk=True, **shape_kw(s))
-    if st.fused:
-        ms_f, _ = time_stack(st, args.steps, args.warmup)
-        st_fi = dsa.Stack(s.pattern, layers, ctx, fused_topk=True, **shape_kw(s, attn=False))
-        ms_fi, _ = time_stack(st_fi, args.steps, args.warmup)
-        res["config"]["fused_topk_ms_per_step"] = ms_f
-        res["config"]["fused_topk_indexer_topk_us_per_layer"] = ms_fi * 1e3 / s.n_layers
-        log(f"config   {ms_f:8.3f} ms/step with the fused indexer + top-k "
-            f"({ms_fi * 1e3 / s.n_layers:.2f} us/layer without attention)")
-        del st_fi
-    del st
+    # ---- the same stack with F layers through the separate indexer (scores
+    # to memory, top-k histogram built on the way) and top-k kernels, for
+    # comparison with the default fused indexer + top-k
+    st = dsa.Stack(s.pattern, layers, ctx, fused_topk=False, **shape_kw(s))
+    ms_u, _ = time_stack(st, args.steps, args.warmup)
+    st_ui = dsa.Stack(s.pattern, layers, ctx, fused_topk=False, **shape_kw(s, attn=False))
+    ms_ui, _ = time_stack(st_ui, args.steps, args.warmup)
+    res["config"]["fused_topk"] = bool(res_fused)
+    res["config"]["separate_topk_ms_per_step"] = ms_u
+    res["config"]["separate_topk_indexer_topk_us_per_layer"] = ms_ui * 1e3 / s.n_layers
+    log(f"config   {ms_u:8.3f} ms/step with separate indexer and top-k kernels "
+        f"({ms_ui * 1e3 / s.n_layers:.2f} us/layer without attention)")
+    del st, st_ui
 
     # ---- per-kernel durations (events around back-to-back launches)
     f_layers = [l for l, c in enumerate(s.pattern) if c == "F"]
@@ -217,6 +217,16 @@ def decode_bench(args, dev):
                         dtype=torch.uint8, device=dev)
     t_topk = event_time_ms(lambda i=0: dsa.topk(score[..., :s.Lmax], ctx, s.k, out=idx,
                                                 workspace=tk_ws), reps)
+    fz_ws = torch.zeros(dsa.indexer_topk_workspace_size(s.B, s.T, s.H, s.D, s.Lmax, s.k,
+                                                        s.idx_dtype),
+                        dtype=torch.uint8, device=dev)
+
+    def run_fused(i=0):
+        L = layers[f_layers[i % len(f_layers)]]
+        dsa.indexer_topk(L["q_idx"], L["w"], L["k_idx"], ctx, s.k, L["q_idx_scale"],
+                         L["k_idx_scale"], out=idx, workspace=fz_ws)
+
+    t_fused = event_time_ms(run_fused, reps)
     at_ws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(s.B, s.T, s.Hq, s.k)),
                         dtype=torch.uint8, device=dev)
 
@@ -229,24 +239,34 @@ def decode_bench(args, dev):
     ib = indexer_bytes(s)
     ab, af = attn_bytes_flops(s)
     nF = s.pattern.count("F")
+    # the default stack runs the fused indexer + top-k; the separate kernels
+    # run only with fused_topk=False (launches_per_step 0 here)
+    fb = ib - s.B * s.T * s.Lmax * 4 + s.B * s.T * s.k * 4  # no score writes; indices out
     kernels = {
-        "indexer_decode": dict(us=t_idx * 1e3, launches_per_step=nF, bytes=ib,
-                               gbs=ib / (t_idx * 1e-3) / 1e9),
-        "topk": dict(us=t_topk * 1e3, launches_per_step=nF,
+        "indexer_topk": dict(us=t_fused * 1e3, launches_per_step=nF if res_fused else 0,
+                             bytes=fb, gbs=fb / (t_fused * 1e-3) / 1e9,
+                             path="default stack: fused indexer + top-k (kernel + finish)"),
+        "indexer_decode": dict(us=t_idx * 1e3, launches_per_step=0 if res_fused else nF,
+                               bytes=ib, gbs=ib / (t_idx * 1e-3) / 1e9,
+                               path="separate path: indexer writing scores"),
+        "topk": dict(us=t_topk * 1e3, launches_per_step=0 if res_fused else nF,
                      bytes=s.B * s.Lmax * 4 + s.B * s.k * 4,
-                     gbs=(s.B * s.Lmax * 4 + s.B * s.k * 4) / (t_topk * 1e-3) / 1e9),
+                     gbs=(s.B * s.Lmax * 4 + s.B * s.k * 4) / (t_topk * 1e-3) / 1e9,
+                     path="separate path: top-k over the scores"),
         "sparse_mla": dict(us=t_attn * 1e3, launches_per_step=s.n_layers, bytes=ab, flops=af,
                            gbs=ab / (t_attn * 1e-3) / 1e9,
                            tflops=af / (t_attn * 1e-3) / 1e12),
     }
     for k_, v in kernels.items():
         v["us_per_step"] = v["us"] * v["launches_per_step"]
+        v.setdefault("path", "")
         log(f"kernel {k_:15s} {v['us']:8.2f} us x {v['launches_per_step']:2d}  "
             f"{v['gbs']:8.1f} GB/s")
     dom = max(kernels, key=lambda n: kernels[n]["us_per_step"])
     kd = kernels[dom]
-    src = {"indexer_decode": "indexer_decode.hip", "sparse_mla": "sparse_mla.hip",
-           "topk": "topk.hip"}[dom]
+    srcs = {"indexer_decode": "indexer_decode.hip", "indexer_topk": "indexer_decode.hip",
+            "sparse_mla": "sparse_mla.hip", "topk": "topk.hip"}
+    src = srcs[dom]
     roof = dict(kernel=dom, bound="hbm", achieved=round(kd["gbs"], 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(kd["gbs"] / HBM_PEAK_GBS, 4),
                 traffic=recorded_traffic(dom, src),
@@ -255,9 +275,7 @@ def decode_bench(args, dev):
         roof["mfma_tflops"] = round(kd["tflops"], 1)
         roof["mfma_frac_bf16"] = round(kd["tflops"] / BF16_PEAK_TFLOPS, 4)
     for name, v in kernels.items():
-        v["traffic"] = recorded_traffic(name, {"indexer_decode": "indexer_decode.hip",
-                                               "sparse_mla": "sparse_mla.hip",
-                                               "topk": "topk.hip"}[name])
+        v["traffic"] = recorded_traffic(name, srcs[name])
     return s, layers, res, cut, kernels, roof
 
 

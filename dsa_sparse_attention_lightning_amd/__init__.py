@@ -341,16 +341,16 @@ class Stack:
 
     def __init__(self, pattern: str, layers: Sequence[Dict], ctx_len, *, B, T, H, D, Lmax, k,
                  Hq=0, idx_dtype="bf16", scale=1.0, d_qk=576, d_v=512, device=None,
-                 fused_topk=False):
+                 fused_topk=True):
         """fused_topk: F layers run indexer_topk (scores kept on chip) where
-        it takes the shape, instead of scores through score_buf + topk."""
+        it takes the shape; False: scores through score_buf, then topk."""
         torch = _torch()
         self.pattern = pattern.encode()
         self.n_layers = len(layers)
         self._keep = [layers, ctx_len]
         self.layers = _layer_array(layers)
         dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
-        flags = _lib.DSA_STACK_FUSED_TOPK if fused_topk else 0
+        flags = 0 if fused_topk else _lib.DSA_STACK_UNFUSED_TOPK
         self.shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale), flags)
         self.ctx_len = ctx_len
         dev = device if device is not None else ctx_len.device

@@ -29,7 +29,7 @@ class StackShape(ctypes.Structure):
                 ("k", c_int), ("Hq", c_int), ("d_qk", c_int), ("d_v", c_int),
                 ("idx_dtype", c_int), ("scale", c_f32), ("flags", c_int)]
 
-DSA_STACK_FUSED_TOPK = 1
+DSA_STACK_UNFUSED_TOPK = 1
 
 
 class StackStats(ctypes.Structure):

@@ -159,7 +159,7 @@ bool fused_topk_applies(int B, int T, int H, int D, dsa_dtype_t dtype, int Lmax,
 }
 
 bool stack_fuses_topk(const dsa_stack_shape_t* s) {
-  return (s->flags & DSA_STACK_FUSED_TOPK) &&
+  return !(s->flags & DSA_STACK_UNFUSED_TOPK) &&
          fused_topk_applies(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k);
 }
 
@@ -436,7 +436,7 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
   }
   const dsa_stack_shape_t& s = *shape;
   CHECK(s.Hq >= 0, DSA_ERR_INVALID_ARG, "%s: Hq must be >= 0", fn);
-  CHECK((s.flags & ~DSA_STACK_FUSED_TOPK) == 0, DSA_ERR_INVALID_ARG, "%s: unknown flags 0x%x",
+  CHECK((s.flags & ~DSA_STACK_UNFUSED_TOPK) == 0, DSA_ERR_INVALID_ARG, "%s: unknown flags 0x%x",
         fn, (unsigned)s.flags);
   const bool fused = stack_fuses_topk(shape);
   size_t need = 0;

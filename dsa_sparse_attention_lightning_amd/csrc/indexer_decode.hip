@@ -33,25 +33,24 @@
 //
 // Fused variant (FUSE): the same kernel feeding the top-k selection without
 // writing scores to memory.  A workgroup's keys (at most kFuseKeys) keep
-// their scores in LDS while the first radix histogram is built.  The
-// workgroup then adds its counts to the row's histogram, meets the row's
-// other workgroups at a per-row barrier, reads the finished histogram, finds
-// the threshold bin b1, and compacts its own keys in bins >= b1 into the
-// candidate slices of its chunks (a chunk is the kDecWaves consecutive tiles
-// that one sweep of the workgroup's waves covers); a finishing kernel then
-// concatenates the slices per row and completes the selection.
+// their scores in LDS while the first radix histogram is built, and the
+// workgroup compacts its own candidates (keys in bins >= a threshold bin)
+// into its slice of the candidate buffer (a workgroup covers one contiguous
+// run of tiles); a finishing kernel then concatenates the slices per row and
+// completes the selection from the row's finished histogram.
 //
-// The barrier needs no cache maintenance: every value that crosses
-// workgroups goes through device-scope atomics.  A workgroup waits for the
-// old values of its histogram adds (so each add has been performed) before
-// it increments the row's arrival word, and a workgroup that has seen every
-// arrival then reads the histogram with device-scope atomic loads.  The wait
-// cannot deadlock: workgroups are dispatched in grid order, the rows are
-// consecutive runs of the grid, and one row's workgroups (at most one per CU)
-// fit on the GPU together, so the rows before a waiting row always finish
-// and make room for the rest of it.  The wait is still bounded: on expiry
-// the top bit of the arrival word is set and the finishing kernel gives the
-// row an empty selection rather than a wrong one.
+// No workgroup waits for another.  The threshold bin only has to be a lower
+// bound of the true one: counts only grow, so the k-th largest key of any
+// part of the row's histogram lies in a bin at or below that of the whole
+// row, and keys in bins at or above it are a superset of the true candidates
+// (the finishing pass never emits the extra ones).  Each wave hands its
+// eighth of the workgroup's bins to the row histogram three quarters of the
+// way through its tiles (an LDS exchange with zero, then device-scope adds);
+// at the end a workgroup reads the row histogram as it stands, adds the
+// counts it has not handed off yet (they cannot be in what it read), takes
+// the threshold bin of that sum, and hands those counts off after the read
+// has returned.  So the bound covers about three quarters of every
+// workgroup's keys plus all of its own.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -70,14 +69,11 @@ constexpr int kNT = 2;
 constexpr int kDeviceScope = 16;  // cache policy sc1: coherent at device scope
 constexpr int kParts = 4;  // independent fma chains of the head sum
 constexpr int kFuseKeys = 8192;        // keys whose scores a fused workgroup keeps in LDS
-constexpr uint32_t kSpinLimit = 1u << 18;  // polls of the row barrier before giving up
 
 // Outputs of the fused variant (chunk slices of the top-k workspace).
 struct FuseArgs {
   int k;                // keys to select per row
   int n_chunks;         // chunks per row (kDecWaves tiles each)
-  uint32_t* arrive;     // per-row arrival words (zero on entry)
-  uint32_t* sel;        // per-row {b1, count above b1, listed}
   uint32_t* cnt;        // per-(row, chunk) candidate counts
   uint32_t* key;        // candidate keys, Lmax per row, chunk c at c * chunk keys
   int32_t* pos;         // candidate positions, same layout
@@ -117,17 +113,25 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   // waves sweep the row together, front to back (measurably closer to plain
   // streaming bandwidth than giving each wave its own contiguous run).  The
   // loop below runs over the wave's sequence numbers j = 0, 1, ...
-  const int first = blockIdx.x * kDecWaves + wave;
-  const int wstride = gridDim.x * kDecWaves;
+  // The fused variant gives each workgroup one contiguous run of
+  // kDecWaves * tiles_per_wave tiles instead (its waves interleaved inside
+  // it), so that its candidates form one position-ordered slice.
+  const int wg_end = FUSE ? min(tiles, (int)(blockIdx.x + 1) * kDecWaves * tiles_per_wave) : tiles;
+  const int first = FUSE ? (int)blockIdx.x * kDecWaves * tiles_per_wave + wave
+                         : (int)blockIdx.x * kDecWaves + wave;
+  const int wstride = FUSE ? kDecWaves : (int)gridDim.x * kDecWaves;
   const int tile0 = 0;
   // (a wave past the row's last tile runs no iteration but stays for the
   // workgroup barriers of the histogram)
-  const int tend = first < tiles ? min(tiles_per_wave, (tiles - first + wstride - 1) / wstride) : 0;
+  const int tend =
+      first < wg_end ? min(tiles_per_wave, (wg_end - first + wstride - 1) / wstride) : 0;
   if (row_hist) {
     for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
     __syncthreads();
   }
   auto tmap = [&](int j) { return __builtin_amdgcn_readfirstlane(first + j * wstride); };
+  // fused: the tile after which a wave hands its bins off (none if < 0)
+  const int hand_off = (3 * tend) / 4 - 1;
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
@@ -253,6 +257,17 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       }
     }
     __builtin_amdgcn_wave_barrier();
+    if constexpr (FUSE) {
+      if (seq == hand_off) {  // this wave's eighth of the bins, counted so far
+        uint32_t* rh = row_hist + (int64_t)row * kHistBins;
+#pragma unroll
+        for (int u = 0; u < kHistBins / kDecWaves / kWave; ++u) {
+          const int i = wave * (kHistBins / kDecWaves) + lane + kWave * u;
+          const uint32_t c = atomicExch(&lhist[i], 0u);
+          if (c) __hip_atomic_fetch_add(&rh[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
   };
   if (tile0 < tend) load(tile0, ba, sa);
   if (tile0 + 1 < tend) load(tile0 + 1, bb, sb);
@@ -279,47 +294,16 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
     constexpr int NT = kDecWaves * kWave;
     constexpr int HV = kHistBins / NT;  // bins per thread
     const int n = (int)max((int64_t)0, min(pos + 1, (int64_t)Lmax));  // visible keys
-    if (n <= fa.k) return;  // the whole row is selected: nothing to meet for
-    __syncthreads();
+    if (n <= fa.k) return;  // the whole row is selected: no candidates needed
+    __syncthreads();  // every tile done; lhist holds the counts not handed off
     uint32_t* rh = row_hist + (int64_t)row * kHistBins;
-    // Add the counts, waiting for every add's old value: each add has then
-    // been performed before the arrival below is.  All adds are issued
-    // before the first old value is used (one round trip, not one each).
+    // A lower bound of the row's histogram: the row histogram as it stands
+    // plus this workgroup's counts not handed off yet.  Thread t owns bins
+    // 4 (t + NT u) .. +3; the 16-byte loads are device-scope (they bypass
+    // this XCD's possibly stale L2 lines, as an atomic load does).
+    constexpr int HV4 = HV / 4;
+    i32x4 own[HV4];
     {
-      uint32_t cv[HV], old[HV];
-#pragma unroll
-      for (int u = 0; u < HV; ++u) cv[u] = lhist[threadIdx.x + NT * u];
-#pragma unroll
-      for (int u = 0; u < HV; ++u) {
-        old[u] = 0;
-        if (cv[u])
-          old[u] = __hip_atomic_fetch_add(&rh[threadIdx.x + NT * u], cv[u], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-      }
-      uint32_t sink = 0;
-#pragma unroll
-      for (int u = 0; u < HV; ++u) sink |= old[u];
-      asm volatile("" ::"v"(sink));
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t* a = fa.arrive + row;
-      __hip_atomic_fetch_add(a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (uint32_t it = 0;; ++it) {
-        if (__hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gridDim.x) break;
-        if (it == kSpinLimit) {
-          __hip_atomic_fetch_or(a, 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    __syncthreads();
-    // The row's finished histogram (16-byte loads at device scope: they
-    // bypass this XCD's possibly stale L2 lines, as an atomic load does),
-    // then its threshold bin.
-    {
-      constexpr int HV4 = HV / 4;
       const __amdgpu_buffer_rsrc_t hr =
           __builtin_amdgcn_make_buffer_rsrc((void*)rh, 0, kHistBins * 4, kBufferWord3);
       i32x4 hv[HV4];
@@ -329,54 +313,63 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
                                               hr, (threadIdx.x + NT * u) * 16, 0, kDeviceScope));
 #pragma unroll
       for (int u = 0; u < HV4; ++u)
-        *reinterpret_cast<i32x4*>(&lhist[4 * (threadIdx.x + NT * u)]) = hv[u];
+        own[u] = *reinterpret_cast<const i32x4*>(&lhist[4 * (threadIdx.x + NT * u)]);
+#pragma unroll
+      for (int u = 0; u < HV4; ++u)
+        *reinterpret_cast<i32x4*>(&lhist[4 * (threadIdx.x + NT * u)]) = hv[u] + own[u];
     }
+    // fewer than k keys counted so far: no bin holds the k-th, and bin 0
+    // (every key a candidate) is the bound
+    if (threadIdx.x == 0) fsel[0] = 0;
     __syncthreads();
     select_bin<kHistBins, NT>(lhist, (uint32_t)fa.k, fscan, fsel);
     const uint32_t b1 = fsel[0];
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      fa.sel[3 * row] = b1;
-      fa.sel[3 * row + 1] = fsel[1];
-      fa.sel[3 * row + 2] = fsel[1] + lhist[b1];
-    }
-    // Ordered compaction: wave w takes the workgroup's chunks w, w + W, ...;
-    // lane l holds PL consecutive keys of the chunk.
-    constexpr int G = kDecWaves * TK;  // keys per chunk
-    constexpr int PL = G / kWave;
-    static_assert(PL % 4 == 0, "whole 16-byte LDS reads per lane");
-    uint32_t* ckr = fa.key + (int64_t)row * Lmax;
-    int32_t* cpr = fa.pos + (int64_t)row * Lmax;
-    for (int j = wave; j < tiles_per_wave; j += kDecWaves) {
-      const int chunk = j * (int)gridDim.x + (int)blockIdx.x;
-      if (chunk >= fa.n_chunks) break;
-      const int p0 = chunk * G + lane * PL;
-      uint32_t key[PL];
-      bool ok[PL];
+    // Hand off the rest; the read above has returned (its values were used),
+    // so it cannot have counted these.
+#pragma unroll
+    for (int u = 0; u < HV4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (own[u][e])
+          __hip_atomic_fetch_add(&rh[4 * (threadIdx.x + NT * u) + e], (uint32_t)own[u][e],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Ordered compaction of the workgroup's keys (sbuf holds them in
+    // position order from p_base) into its slice, 8 consecutive keys per
+    // thread per pass.
+    const int keys_wg = kDecWaves * tiles_per_wave * TK;
+    const int p_base = (int)blockIdx.x * keys_wg;
+    uint32_t* ck = fa.key + (int64_t)row * Lmax + p_base;
+    int32_t* cp = fa.pos + (int64_t)row * Lmax + p_base;
+    uint32_t run = 0;
+    for (int b0 = 0; b0 < keys_wg; b0 += NT * 8) {
+      const int l0 = b0 + (int)threadIdx.x * 8;
+      const bool mine = l0 < keys_wg;  // keys_wg is a multiple of 8
+      uint32_t key[8];
+      bool ok[8];
       uint32_t c = 0;
+      const float4 f0 = mine ? *reinterpret_cast<const float4*>(&sbuf[l0]) : float4{};
+      const float4 f1 = mine ? *reinterpret_cast<const float4*>(&sbuf[l0 + 4]) : float4{};
+      key[0] = float_key(f0.x); key[1] = float_key(f0.y);
+      key[2] = float_key(f0.z); key[3] = float_key(f0.w);
+      key[4] = float_key(f1.x); key[5] = float_key(f1.y);
+      key[6] = float_key(f1.z); key[7] = float_key(f1.w);
 #pragma unroll
-      for (int v = 0; v < PL / 4; ++v) {
-        const float4 f = *reinterpret_cast<const float4*>(&sbuf[j * G + lane * PL + 4 * v]);
-        key[4 * v] = float_key(f.x);
-        key[4 * v + 1] = float_key(f.y);
-        key[4 * v + 2] = float_key(f.z);
-        key[4 * v + 3] = float_key(f.w);
-      }
-#pragma unroll
-      for (int e = 0; e < PL; ++e) {
-        ok[e] = (p0 + e) < n && (key[e] >> (32 - kHistBits)) >= b1;
+      for (int e = 0; e < 8; ++e) {
+        ok[e] = mine && (p_base + l0 + e) < n && (key[e] >> (32 - kHistBits)) >= b1;
         c += ok[e];
       }
-      const uint32_t incl = wave_incl_scan(c);
-      uint32_t at = chunk * G + incl - c;
+      uint32_t tot;
+      uint32_t at = run + block_excl_scan<kDecWaves>(c, fscan, tot);
 #pragma unroll
-      for (int e = 0; e < PL; ++e)
+      for (int e = 0; e < 8; ++e)
         if (ok[e]) {
-          ckr[at] = key[e];
-          cpr[at] = p0 + e;
+          ck[at] = key[e];
+          cp[at] = p_base + l0 + e;
           ++at;
         }
-      if (lane == kWave - 1) fa.cnt[(int64_t)row * fa.n_chunks + chunk] = incl;
+      run += tot;
     }
+    if (threadIdx.x == 0) fa.cnt[(int64_t)row * fa.n_chunks + blockIdx.x] = run;
   }
 }
 
@@ -406,7 +399,8 @@ DecPlan plan_fused(int rows, int D, bool fp8, int Lmax) {
   const int tk = kTileBytes / (D * (fp8 ? 1 : 2));
   return plan_dec(rows, D, fp8, Lmax, kFuseKeys / (kDecWaves * tk));
 }
-int fused_chunks(const DecPlan& p) { return (p.tiles + kDecWaves - 1) / kDecWaves; }
+// The fused variant's chunks are its workgroups' runs of tiles.
+int fused_chunks(const DecPlan& p) { return p.gx; }
 
 template <int D, bool FP8, int HB, bool FUSE>
 hipError_t launch_dec(const DecPlan& p, const void* q, const float* q_scale, const float* w,
@@ -469,19 +463,15 @@ hipError_t launch_indexer_topk_decode(const void* q, bool fp8, const float* q_sc
   const DecPlan p = plan_fused(rows, D, fp8, Lmax);
   const int n_chunks = fused_chunks(p);
   if (n_chunks > kTopkMaxChunks) return hipErrorInvalidValue;
-  // One row's workgroups must fit on the GPU together (one per CU).
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  if (p.gx > cus) return hipErrorInvalidConfiguration;
   const TopkWs ws = topk_chunk_ws(workspace, rows, Lmax, n_chunks);
-  const FuseArgs fa{k_sel, n_chunks, ws.arrive, ws.sel, ws.cnt, ws.key, ws.pos};
-  e = dispatch_dec<true>(p, q, fp8, q_scale, w, k, k_scale, ctx_len, rows, T, H, D, Lmax,
-                         nullptr, 0, ws.hist, fa, stream);
+  const FuseArgs fa{k_sel, n_chunks, ws.cnt, ws.key, ws.pos};
+  hipError_t e = dispatch_dec<true>(p, q, fp8, q_scale, w, k, k_scale, ctx_len, rows, T, H, D,
+                                    Lmax, nullptr, 0, ws.hist, fa, stream);
   if (e != hipSuccess) return e;
-  return launch_topk_finish(nullptr, 0, ctx_len, B, T, Lmax, k_sel, kDecWaves * p.tk, n_chunks,
-                            ws, idx, stream);
+  // no score row in memory, and the threshold is taken from the finished
+  // histogram (the fused kernel's was only a lower bound)
+  return launch_topk_finish(nullptr, 0, ctx_len, B, T, Lmax, k_sel, kDecWaves * p.tpw * p.tk,
+                            n_chunks, ws, true, idx, stream);
 }
 
 }  // namespace dsa

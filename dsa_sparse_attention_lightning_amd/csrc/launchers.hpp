@@ -36,14 +36,13 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
                        bool hist_ready, hipStream_t stream);
 
 // Workspace of the chunked (few long rows) selection, in order: per-row
-// 4096-bin histograms and arrival words (zero before the first call, left
-// zero by every call), per-row selection {b1, count above b1, listed},
-// per-chunk candidate counts, candidate keys and positions (Lmax per row;
-// chunk c's slice starts at c * chunk).
+// 4096-bin histograms (zero before the first call, left zero by every call),
+// per-row selection {b1, count above b1, listed}, per-chunk candidate counts,
+// candidate keys and positions (Lmax per row; chunk c's slice starts at
+// c * chunk).
 constexpr int kTopkMaxChunks = 1024;
 struct TopkWs {
   uint32_t* hist;
-  uint32_t* arrive;
   uint32_t* sel;
   uint32_t* cnt;
   uint32_t* key;
@@ -52,17 +51,20 @@ struct TopkWs {
 size_t topk_chunk_ws_bytes(int rows, int Lmax, int n_chunks);
 TopkWs topk_chunk_ws(void* ws, int rows, int Lmax, int n_chunks);
 // Steps 3-4 of the selection from chunk slices already in w (one workgroup
-// per row); scores may be null when no score row exists in memory.
+// per row); scores may be null when no score row exists in memory.  With
+// sel_from_hist the threshold bin is taken from the finished row histogram
+// and the slices may hold extra entries below it; otherwise w.sel holds the
+// row's selection and the slices exactly the keys in bins >= it.
 hipError_t launch_topk_finish(const float* scores, int64_t ld, const int32_t* ctx_len, int B,
                               int T, int Lmax, int k, int chunk, int n_chunks, const TopkWs& w,
-                              int32_t* idx, hipStream_t stream);
+                              bool sel_from_hist, int32_t* idx, hipStream_t stream);
 
 // Fused decode indexer + top-k: the indexer keeps each workgroup's scores in
-// LDS, builds the selection's first histogram, meets the row's other
-// workgroups at a per-row barrier, and compacts its own candidates; the
-// finishing workgroup per row then completes the selection.  Scores never
-// reach memory.  Supported when the decode indexer runs (not the prefill
-// kernel) and the plan fits (see indexer_topk_plan_ok); workspace as above.
+// LDS, builds the selection's first histogram, compacts its own candidates
+// against a lower bound of the threshold bin, and the finishing workgroup
+// per row completes the selection.  Scores never reach memory.  Supported
+// when the decode indexer runs (not the prefill kernel) and the plan fits
+// (see indexer_topk_plan_ok); workspace as above.
 bool indexer_topk_plan_ok(int B, int T, int D, bool fp8, int Lmax, int k);
 size_t indexer_topk_workspace_bytes(int B, int T, int D, bool fp8, int Lmax, int k);
 hipError_t launch_indexer_topk_decode(const void* q, bool fp8, const float* q_scale,

@@ -22,11 +22,12 @@
 //     atomics into a per-row histogram), a second compacts each chunk's
 //     candidates in order into its own slice of a candidate buffer, and a
 //     per-row workgroup concatenates the slices and finishes 3-4.  The
-//     per-row histogram (and the arrival word that the fused decode indexer
-//     meets at) is cleared again by that last kernel, so the workspace
-//     holding them must be zero before the first call and is left zero by
-//     every call.  The fused decode indexer produces the histogram and the
-//     slices itself and runs only the finishing kernel.
+//     per-row histogram is cleared again by that last kernel, so the
+//     workspace holding it must be zero before the first call and is left
+//     zero by every call.  The fused decode indexer produces the histogram
+//     and the slices itself (against a lower bound of the threshold bin)
+//     and runs only the finishing kernel, which then takes the threshold
+//     from the finished histogram.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -461,17 +462,18 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
   if (tid == 0) cand_cnt[(int64_t)row * n_chunks + blockIdx.x] = (c0 < c1) ? run : 0u;
 }
 
-// Steps 3-4 for one row from the chunk slices; clears the row's histogram
-// and arrival word.  scores is null after the fused indexer (no score row in
-// memory): an overflowing list is then read from the slices.  A row whose
-// arrival word has its top bit set (the fused indexer's row barrier gave up
-// waiting) gets an empty selection (all -1).
+// Steps 3-4 for one row from the chunk slices; clears the row's histogram.
+// scores is null after the fused indexer (no score row in memory): an
+// overflowing list is then read from the slices.  With sel_from_hist (after
+// the fused indexer) the threshold bin comes from the finished histogram and
+// the slices may also hold keys below it, which are never emitted; otherwise
+// row_sel holds it (written by the collect pass).
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
     int Lmax, int k, int chunk, int n_chunks, uint32_t* __restrict__ hist_g,
-    uint32_t* __restrict__ arrive, const uint32_t* __restrict__ cand_key,
-    const int32_t* __restrict__ cand_pos, const uint32_t* __restrict__ cand_cnt,
-    const uint32_t* __restrict__ row_sel, int32_t* __restrict__ idx) {
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
+    const uint32_t* __restrict__ cand_cnt, const uint32_t* __restrict__ row_sel,
+    bool sel_from_hist, int32_t* __restrict__ idx) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
   const int tid = threadIdx.x;
@@ -479,14 +481,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   const int n = visible(ctx_len, row, T, Lmax);
   int32_t* out = idx + (int64_t)row * k;
   uint32_t* hg = hist_g + (int64_t)row * kBins1;
-  const uint32_t arrived = arrive[row];
-  __syncthreads();  // every thread has read the word before it is cleared
-  if (tid == 0) arrive[row] = 0u;
-  if (arrived & 0x80000000u) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = -1;
-    for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
-    return;
-  }
   if (n <= k) {
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     // the chunk kernels touched nothing for this row, but a fused
@@ -494,11 +488,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
     return;
   }
-  // the row's selection (written by the collect pass) and the slice counts
+  // the slice counts, and the row's selection (written by the collect pass)
   const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
-  const uint32_t b1 = row_sel[3 * row];
-  const uint32_t above1 = row_sel[3 * row + 1];
-  const uint32_t listed = row_sel[3 * row + 2];
+  uint32_t b1 = 0, above1 = 0, listed = 0;
+  i32x4 hv = {0, 0, 0, 0};
+  static_assert(kBins1 == 4 * kTkThreads, "one 16-byte histogram load per thread");
+  if (sel_from_hist)
+    hv = ld16(hg + 4 * tid);
+  else {
+    b1 = row_sel[3 * row];
+    above1 = row_sel[3 * row + 1];
+    listed = row_sel[3 * row + 2];
+  }
   // Each slice is copied by its own group of tpc threads.  The first batch
   // of every slice is requested now, before its length is known (slice c
   // starts at c * chunk; entries past its length are ignored), so the copy
@@ -518,7 +519,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     kv[u] = ck[e];
     pv[u] = cp[e];
   }
-  for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;  // ready for the next call
+  if (sel_from_hist) {  // the threshold bin of the finished histogram
+    *reinterpret_cast<i32x4*>(&sm.hist[4 * tid]) = hv;
+    __syncthreads();
+    select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
+    b1 = sm.sel[0];
+    above1 = sm.sel[1];
+  }
+  // ready for the next call (every thread's histogram load has returned)
+  *reinterpret_cast<i32x4*>(hg + 4 * tid) = i32x4{0, 0, 0, 0};
   // concatenate the chunk slices in chunk order: prefix sum of the slice
   // counts, then each slice is copied by its own group of tpc threads
   {
@@ -526,6 +535,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     const uint32_t ex = block_excl_scan<kTkWaves>(cnt, sm.scan, tot);
     if (tid < n_chunks) sm.chunk_off[tid] = ex;
     if (tid == 0) sm.chunk_off[n_chunks] = tot;
+    if (sel_from_hist) listed = tot;  // every slice entry, extra ones included
   }
   __syncthreads();
   if (listed > (uint32_t)kTkCap) {
@@ -595,16 +605,14 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-// Workspace of the chunked selection: per-row histograms and arrival words
-// (kept zero between calls), per-row selection {b1, count above b1, listed},
-// per-chunk counts, candidate keys and positions.
+// Workspace of the chunked selection: per-row histograms (kept zero between
+// calls), per-row selection {b1, count above b1, listed}, per-chunk counts,
+// candidate keys and positions.
 TopkWs topk_chunk_ws(void* ws, int rows, int Lmax, int n_chunks) {
   unsigned char* p = reinterpret_cast<unsigned char*>(ws);
   TopkWs w;
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins1 * 4);
-  w.arrive = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * 4);
   w.sel = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * 3 * 4);
   w.cnt = reinterpret_cast<uint32_t*>(p);
@@ -616,8 +624,7 @@ TopkWs topk_chunk_ws(void* ws, int rows, int Lmax, int n_chunks) {
 }
 
 size_t topk_chunk_ws_bytes(int rows, int Lmax, int n_chunks) {
-  return align256((size_t)rows * kBins1 * 4) + align256((size_t)rows * 4) +
-         align256((size_t)rows * 3 * 4) + align256((size_t)rows * n_chunks * 4) +
+  return align256((size_t)rows * kBins1 * 4) + align256((size_t)rows * 3 * 4) + align256((size_t)rows * n_chunks * 4) +
          2 * align256((size_t)rows * Lmax * 4);
 }
 
@@ -664,19 +671,19 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
                      w.sel);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_finish(scores, ld, ctx_len, B, T, Lmax, k, p.chunk, p.n_chunks, w, idx,
-                            stream);
+  return launch_topk_finish(scores, ld, ctx_len, B, T, Lmax, k, p.chunk, p.n_chunks, w, false,
+                            idx, stream);
 }
 
 hipError_t launch_topk_finish(const float* scores, int64_t ld, const int32_t* ctx_len, int B,
                               int T, int Lmax, int k, int chunk, int n_chunks, const TopkWs& w,
-                              int32_t* idx, hipStream_t stream) {
+                              bool sel_from_hist, int32_t* idx, hipStream_t stream) {
   const size_t smem = sizeof(TopkSmem);
   hipError_t e = set_smem_attr((const void*)topk_finish_kernel, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_finish_kernel, dim3(B * T), dim3(kTkThreads), smem, stream, scores, ld,
-                     ctx_len, T, Lmax, k, chunk, n_chunks, w.hist, w.arrive, w.key, w.pos, w.cnt,
-                     w.sel, idx);
+                     ctx_len, T, Lmax, k, chunk, n_chunks, w.hist, w.key, w.pos, w.cnt, w.sel,
+                     sel_from_hist, idx);
   return hipGetLastError();
 }
 

@@ -113,23 +113,20 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx
  * idx [B,T,k_sel] is exactly what dsa_indexer_scores followed by dsa_topk
  * write for the same inputs (the same fp32 scores decide the same
  * selection), but the scores never reach memory: each workgroup keeps its
- * keys' scores in LDS, the workgroups of a row meet at a per-row barrier in
- * the workspace (device-scope atomics only) and each compacts its own
- * candidates, then one workgroup per row completes the selection.
+ * keys' scores in LDS and compacts its own candidates against a lower bound
+ * of the row's threshold (taken from the row histogram in the workspace as
+ * it stands, no workgroup waiting for another), then one workgroup per row
+ * completes the selection from the finished histogram.
  * Arguments are those of dsa_indexer_scores and dsa_topk (k_sel is dsa_topk's
  * k), with the same limits.
  * Supported where the one-query-row indexer kernel runs (T == 1, or H / D
  * that the prefill kernel does not take) and a row splits into at most 1024
- * chunks of eight 8 KB key tiles (Lmax up to 524288 fp8 keys at D = 128);
+ * workgroups (Lmax up to 8388608 fp8 keys at D = 128);
  * dsa_indexer_topk_workspace_size returns DSA_ERR_UNSUPPORTED otherwise.
  * workspace: dsa_indexer_topk_workspace_size bytes (device), zero-filled
- * before its first use; every call leaves its leading histograms and
- * arrival words zero again.  Its layout starts like dsa_topk's, so one
- * zero-filled buffer of the larger size serves both.  Calls sharing a
- * workspace must not run concurrently.  The barrier needs one row's
- * workgroups (at most one per CU) resident together; should that not happen
- * within a bounded wait (another kernel holding the GPU), the row gets an
- * all -1 selection instead of a hang.
+ * before its first use; every call leaves its leading histograms zero
+ * again.  Its layout is dsa_topk's, so one zero-filled buffer of the larger
+ * size serves both.  Calls sharing a workspace must not run concurrently.
  */
 dsa_status_t dsa_indexer_topk_workspace_size(int B, int T, int H, int D, dsa_dtype_t dtype,
                                              int Lmax, int k_sel, size_t* bytes);
@@ -219,14 +216,14 @@ typedef struct dsa_layer {
 } dsa_layer_t;
 
 /* dsa_stack_shape_t.flags */
-#define DSA_STACK_FUSED_TOPK 1 /* F layers: dsa_indexer_topk where it applies */
+#define DSA_STACK_UNFUSED_TOPK 1 /* F layers: scores through score_buf, then top-k */
 
 typedef struct dsa_stack_shape {
   int B, T, H, D, Lmax, k;
   int Hq, d_qk, d_v;       /* Hq == 0: indexer + top-k only, no attention */
   dsa_dtype_t idx_dtype;
   float scale;             /* softmax scale of the sparse attention       */
-  int flags;               /* 0 or DSA_STACK_FUSED_TOPK                   */
+  int flags;               /* 0 or DSA_STACK_UNFUSED_TOPK                 */
 } dsa_stack_shape_t;
 
 typedef struct dsa_stack_stats {
@@ -242,9 +239,10 @@ typedef struct dsa_stack_stats {
  * nothing to inherit and is rejected).  For layer l:
  *   'F': scores = dsa_indexer_scores(layer l) into score_buf, then
  *        dsa_topk into idx_buf              (the index cache is written);
- *        with DSA_STACK_FUSED_TOPK in flags and a shape dsa_indexer_topk
- *        takes, dsa_indexer_topk into idx_buf instead (the same set;
- *        score_buf is then neither written nor needed and may be NULL)
+ *        where dsa_indexer_topk takes the shape and flags does not hold
+ *        DSA_STACK_UNFUSED_TOPK, dsa_indexer_topk into idx_buf instead
+ *        (the same set; score_buf is then neither written nor needed and
+ *        may be NULL)
  *   'S': nothing                            (idx_buf is reused in place)
  *   then, if Hq > 0, dsa_sparse_attn(layer l, idx_buf).
  * idx_buf [B,T,k] int32 holds the last F layer's set when the call returns.

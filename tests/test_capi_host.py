@@ -224,18 +224,19 @@ def test_header_is_plain_c_and_links(lib, tmp_path):
 
 def test_fused_indexer_topk_host_checks(lib):
     """The fused indexer + top-k takes one-query-row shapes whose rows split
-    into at most 1024 chunks, sizes its workspace like the chunked top-k
-    (plus the larger chunk-count array), and rejects bad calls on the host."""
+    into at most 1024 workgroup runs, sizes its workspace like the chunked
+    top-k (one chunk per workgroup), and rejects bad calls on the host."""
     need = ctypes.c_size_t()
     ws = lib.dsa_indexer_topk_workspace_size
     assert ws(8, 1, 64, 128, _lib.DSA_FP8_E4M3, 131072, 2048, ctypes.byref(need)) == 0
-    rows, L, chunks = 8, 131072, 131072 // 64 // 8
+    rows, L, chunks = 8, 131072, 32   # one chunk per workgroup: 8 waves x 8 tiles of 64 keys
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need.value == (a(rows * 4096 * 4) + a(rows * 4) + a(rows * 12) + a(rows * chunks * 4)
+    assert need.value == (a(rows * 4096 * 4) + a(rows * 12) + a(rows * chunks * 4)
                           + 2 * a(rows * L * 4))
-    # 524288 fp8 keys of D = 128 are 1024 chunks; one more tile is not taken
-    assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 524288, 2048, ctypes.byref(need)) == 0
-    assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 524288 + 64, 2048,
+    # 8388608 fp8 keys of D = 128 are 1024 workgroups of 128 tiles; one more
+    # tile is not taken
+    assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 8388608, 2048, ctypes.byref(need)) == 0
+    assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 8388608 + 64, 2048,
               ctypes.byref(need)) == _lib.DSA_ERR_UNSUPPORTED
     # several query rows per sequence run the prefill indexer: not fused
     assert ws(1, 16, 64, 128, _lib.DSA_FP8_E4M3, 8192, 2048,

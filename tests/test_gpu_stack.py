@@ -118,14 +118,16 @@ def test_bad_pattern_rejected_before_launch(bad):
     assert e.value.status == 1
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("idx_dtype", ["fp8", "bf16"])
-def test_stack_fused_histogram_ragged(idx_dtype):
+def test_stack_fused_histogram_ragged(idx_dtype, fused):
     """Long rows take the chunked top-k, whose first histogram the decode
     indexer builds inside the stack.  Rows with n <= k (every visible position
     kept) and consecutive F layers must leave that histogram clean: each F
     layer's set equals the standalone kernels' (indexer, then top-k with its
     own histogram pass), for every row, and a second run of the same stack
-    reproduces it."""
+    reproduces it.  Both stack paths: the separate indexer (histogram built
+    on the way) + top-k, and the fused indexer + top-k."""
     s = gen.Shape(90, "fused histogram", 3, "FFS", B=3, T=1, ctx=32768, H=16, D=128,
                   idx_dtype=idx_dtype, k=2048, Hq=0)
     say("stack with fused histogram,", idx_dtype)
@@ -141,7 +143,8 @@ def test_stack_fused_histogram_ragged(idx_dtype):
     for run in range(2):
         for p in ("FFS", "FSF"):
             st = dsa.Stack(p, layers, ctx_t, B=s.B, T=1, H=s.H, D=s.D, Lmax=s.Lmax, k=s.k, Hq=0,
-                           idx_dtype=s.idx_dtype, scale=s.scale)
+                           idx_dtype=s.idx_dtype, scale=s.scale, fused_topk=fused)
+            assert st.fused == fused
             st.run()
             torch.cuda.synchronize()
             last_f = max(i for i, c in enumerate(p) if c == "F")
