@@ -60,6 +60,8 @@ CASES = [
     (1, 8, 128, 524288, [524288], 2048, "fp8", "random"),         # 256 workgroups per row
     (1, 4, 128, 8388608, [8388608], 2048, "fp8", "random"),       # 1024: the largest plan
     (1, 64, 128, 100, [100], 64, "fp8", "random"),                # one key tile
+    (1, 64, 128, 65536, [65536], 16384, "fp8", "random"),         # k above the LDS list
+    (2, 64, 64, 10000, [10000, 9000], 8192, "bf16", "random"),    # k close to n
 ]
 
 
