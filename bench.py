@@ -342,16 +342,25 @@ def prefill_bench(dev, reps=5):
         t_i = event_time_ms(lambda i=0: dsa.indexer_scores(qi.q, qi.w, ki.k, ctx, qi.q_scale,
                                                            ki.k_scale, out=score), reps, 1)
         t_k = event_time_ms(lambda i=0: dsa.topk(score[..., :s.Lmax], ctx, s.k, out=idx), reps, 1)
+        # the fused form (scores never written; candidate lists per row)
+        fz_ws = torch.empty(dsa.indexer_topk_workspace_size(s.B, s.T, s.H, s.D, s.Lmax, s.k, dt),
+                            dtype=torch.uint8, device=dev)
+        t_f = event_time_ms(lambda i=0: dsa.indexer_topk(qi.q, qi.w, ki.k, ctx, s.k, qi.q_scale,
+                                                         ki.k_scale, out=idx, workspace=fz_ws),
+                            reps, 1)
+        del fz_ws
         pos0 = s.ctx - s.T
         pairs = sum(pos0 + t + 1 for t in range(s.T))
         flops = 2.0 * s.H * s.D * pairs * s.B
         tf = flops / (t_i * 1e-3) / 1e12
         out[dt] = dict(indexer_ms=round(t_i, 4), topk_ms=round(t_k, 4),
+                       fused_indexer_topk_ms=round(t_f, 4),
                        algorithmic_tflop=round(flops / 1e12, 4), tflops=round(tf, 1),
                        frac_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4),
                        frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
         log(f"prefill {dt}: indexer {t_i:.3f} ms ({tf:.0f} TFLOP/s, "
-            f"{tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak), top-k {t_k:.3f} ms")
+            f"{tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak), top-k {t_k:.3f} ms, fused indexer + "
+            f"top-k {t_f:.3f} ms")
         del qi, ki, score, idx
         torch.cuda.empty_cache()
     return out

@@ -134,7 +134,7 @@ def indexer_topk_workspace_size(B: int, T: int, H: int, D: int, Lmax: int, k: in
 
 def indexer_topk(q, w, k_cache, ctx_len, k: int, q_scale=None, k_scale=None, out=None,
                  workspace=None, stream=None):
-    """Indexer scores and top-k in one pass for decode shapes: [B,T,k] int32.
+    """Indexer scores and top-k in one pass: [B,T,k] int32.
 
     The same set as topk(indexer_scores(q, w, k_cache, ...), ctx_len, k), with
     the scores kept on chip.  A reused `workspace` (uint8 device tensor of
@@ -328,14 +328,6 @@ def greedy_search(cost, n_shared: int):
     return [(raw[m * (n + 1): m * (n + 1) + n].decode(), totals[m]) for m in range(n_shared)]
 
 
-def _fused_applies(B, T, H, D, Lmax, k, idx_dtype) -> bool:
-    try:
-        indexer_topk_workspace_size(B, T, H, D, Lmax, k, idx_dtype)
-        return True
-    except DSAError:
-        return False
-
-
 class Stack:
     """Pre-marshalled arguments of indexcache_run_stack for repeated calls."""
 
@@ -356,7 +348,10 @@ class Stack:
         dev = device if device is not None else ctx_len.device
         self.ld = ld_for(Lmax)
         self.idx_buf = torch.empty((B, T, k), dtype=torch.int32, device=dev)
-        self.fused = fused_topk and _fused_applies(B, T, H, D, Lmax, k, idx_dtype)
+        fz = ctypes.c_int(0)
+        _lib.check(library().indexcache_stack_fuses_topk(ctypes.byref(self.shape),
+                                                         ctypes.byref(fz)))
+        self.fused = bool(fz.value)
         # the fused path never writes scores, so it needs no score buffer
         self.score_buf = None if self.fused else torch.empty((B, T, self.ld),
                                                              dtype=torch.float32, device=dev)

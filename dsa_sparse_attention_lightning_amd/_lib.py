@@ -54,6 +54,8 @@ SIGNATURES = {
     "dsa_kv_append": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_vp,
                               c_vp, c_vp, c_vp]),
     "indexcache_stack_workspace_size": (c_int, [ctypes.POINTER(StackShape), c_size_p]),
+    "indexcache_stack_fuses_topk": (c_int, [ctypes.POINTER(StackShape),
+                                            ctypes.POINTER(ctypes.c_int)]),
     "indexcache_run_stack": (c_int, [ctypes.c_char_p, c_int, ctypes.POINTER(Layer),
                                      ctypes.POINTER(StackShape), c_vp, c_vp, c_vp, c_i64, c_vp,
                                      ctypes.c_size_t, ctypes.POINTER(StackStats), c_vp]),

@@ -151,15 +151,36 @@ dsa_status_t check_attn(const char* fn, const void* q, const void* kv, const int
 // calls) followed by the attention region.
 bool uses_prefill_indexer(int T, int H, int D) { return T > 1 && dsa::indexer_prefill_supported(H, D); }
 
-// The fused indexer + top-k applies: the decode indexer kernel runs for this
-// shape and its chunk plan fits the finishing kernel.
+// The fused indexer + top-k applies: every prefill shape of the prefill
+// kernel, and decode shapes whose workgroup plan fits the finishing kernel.
 bool fused_topk_applies(int B, int T, int H, int D, dsa_dtype_t dtype, int Lmax, int k) {
-  return !uses_prefill_indexer(T, H, D) &&
+  return uses_prefill_indexer(T, H, D) ||
          dsa::indexer_topk_plan_ok(B, T, D, dtype == DSA_FP8_E4M3, Lmax, k);
 }
 
+size_t fused_topk_bytes(int B, int T, int H, int D, dsa_dtype_t dtype, int Lmax, int k) {
+  return uses_prefill_indexer(T, H, D)
+             ? dsa::indexer_topk_prefill_workspace_bytes(B, T, Lmax)
+             : dsa::indexer_topk_workspace_bytes(B, T, D, dtype == DSA_FP8_E4M3, Lmax, k);
+}
+
+hipError_t launch_fused_topk(const void* q, dsa_dtype_t dtype, const float* q_scale,
+                             const float* w, const void* k, const float* k_scale,
+                             const int32_t* ctx_len, int B, int T, int H, int D, int Lmax,
+                             int k_sel, int32_t* idx, void* workspace, hipStream_t stream) {
+  const bool fp8 = dtype == DSA_FP8_E4M3;
+  if (uses_prefill_indexer(T, H, D))
+    return dsa::launch_indexer_topk_prefill(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D,
+                                            Lmax, k_sel, idx, workspace, stream);
+  return dsa::launch_indexer_topk_decode(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D,
+                                         Lmax, k_sel, idx, workspace, stream);
+}
+
+// The stack fuses decode F layers only: for prefill chunks the fused form
+// is slower than the separate kernels on the benchmark's scores (its running
+// bound lists about a quarter of each row) and needs 8 bytes per key per row.
 bool stack_fuses_topk(const dsa_stack_shape_t* s) {
-  return !(s->flags & DSA_STACK_UNFUSED_TOPK) &&
+  return !(s->flags & DSA_STACK_UNFUSED_TOPK) && !uses_prefill_indexer(s->T, s->H, s->D) &&
          fused_topk_applies(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k);
 }
 
@@ -167,10 +188,9 @@ bool stack_fuses_topk(const dsa_stack_shape_t* s) {
 // start with the same zero-kept histograms and arrival words).
 size_t topk_region(const dsa_stack_shape_t* s) {
   size_t b = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
-  if (fused_topk_applies(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k))
-    b = std::max(b, dsa::indexer_topk_workspace_bytes(s->B, s->T, s->D,
-                                                      s->idx_dtype == DSA_FP8_E4M3, s->Lmax,
-                                                      s->k));
+  if (!uses_prefill_indexer(s->T, s->H, s->D) &&
+      fused_topk_applies(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k))
+    b = std::max(b, fused_topk_bytes(s->B, s->T, s->H, s->D, s->idx_dtype, s->Lmax, s->k));
   return (b + 255) & ~size_t(255);
 }
 
@@ -304,10 +324,10 @@ dsa_status_t dsa_indexer_topk_workspace_size(int B, int T, int H, int D, dsa_dty
   CHECK(dtype == DSA_BF16 || dtype == DSA_FP8_E4M3, DSA_ERR_INVALID_ARG, "%s: unknown dtype %d",
         fn, (int)dtype);
   CHECK(fused_topk_applies(B, T, H, D, dtype, Lmax, k), DSA_ERR_UNSUPPORTED,
-        "%s: no fused plan for B=%d T=%d H=%d D=%d Lmax=%d (prefill shapes and more than %d "
-        "chunks per row use dsa_indexer_scores + dsa_topk)",
+        "%s: no fused plan for B=%d T=%d H=%d D=%d Lmax=%d (a decode row split into more "
+        "than %d workgroups: use dsa_indexer_scores + dsa_topk)",
         fn, B, T, H, D, Lmax, dsa::kTopkMaxChunks);
-  *bytes = dsa::indexer_topk_workspace_bytes(B, T, D, dtype == DSA_FP8_E4M3, Lmax, k);
+  *bytes = fused_topk_bytes(B, T, H, D, dtype, Lmax, k);
   return ok();
 }
 
@@ -328,9 +348,8 @@ dsa_status_t dsa_indexer_topk(const void* q, dsa_dtype_t dtype, const float* q_s
   CHECK(workspace_bytes >= need, DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given",
         fn, need, workspace_bytes);
   CHECK_PTR(workspace);
-  return hip_status(dsa::launch_indexer_topk_decode(q, dtype == DSA_FP8_E4M3, q_scale, w, k,
-                                                    k_scale, ctx_len, B, T, H, D, Lmax, k_sel,
-                                                    idx, workspace, stream),
+  return hip_status(launch_fused_topk(q, dtype, q_scale, w, k, k_scale, ctx_len, B, T, H, D,
+                                     Lmax, k_sel, idx, workspace, stream),
                     "fused indexer + top-k launch");
 }
 
@@ -422,6 +441,13 @@ dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* s, size_t*
   return ok();
 }
 
+dsa_status_t indexcache_stack_fuses_topk(const dsa_stack_shape_t* s, int* fused) {
+  const char* fn = "indexcache_stack_fuses_topk";
+  CHECK(s != nullptr && fused != nullptr, DSA_ERR_INVALID_ARG, "%s: NULL argument", fn);
+  *fused = stack_fuses_topk(s) ? 1 : 0;
+  return ok();
+}
+
 dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_layer_t* layers,
                                   const dsa_stack_shape_t* shape, const int32_t* ctx_len,
                                   int32_t* idx_buf, float* score_buf, int64_t ld_scores,
@@ -480,9 +506,9 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
     const dsa_layer_t& L = layers[l];
     if (pattern[l] == 'F' && fused) {  // Full layer, scores kept on chip
       dsa_status_t st = hip_status(
-          dsa::launch_indexer_topk_decode(L.q_idx, s.idx_dtype == DSA_FP8_E4M3, L.q_idx_scale,
-                                          L.w, L.k_idx, L.k_idx_scale, ctx_len, s.B, s.T, s.H,
-                                          s.D, s.Lmax, s.k, idx_buf, workspace, stream),
+          launch_fused_topk(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx, L.k_idx_scale,
+                            ctx_len, s.B, s.T, s.H, s.D, s.Lmax, s.k, idx_buf, workspace,
+                            stream),
           "fused indexer + top-k launch");
       if (st != DSA_OK) return st;
       st_local.n_indexer_calls++;

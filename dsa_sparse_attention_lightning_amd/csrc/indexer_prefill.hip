@@ -18,6 +18,19 @@
 //   * causality: a workgroup never computes keys beyond its last query's
 //     position; those columns, and columns past each query's own position,
 //     are written as -inf.
+//
+// Fused variant (FUSE, feeding the top-k without writing scores): a
+// workgroup takes its 8 query rows over all their keys, so each wave owns
+// one row.  The wave counts its visible scores' top 11 key bits in its own
+// LDS histogram (one workgroup per CU, two waves per SIMD: the eight 8.5 KB
+// histograms and the key tiles fill 105 KB) and, every 4 tiles, takes the
+// bin holding the k-th largest
+// count so far as its row's bound: the k-th largest of the keys seen so far
+// is at most the row's, so every key of the row's top k lies in a bin at or
+// above any bound taken on the way.  Scores in bins at or above the current
+// bound are appended, in position order, to the row's candidate list (a
+// wave-wide ballot gives each its slot); a per-row kernel then selects the
+// top k among the candidates.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -30,17 +43,61 @@ constexpr int kPfTile = 128;   // keys per LDS tile
 constexpr int kParts = 4;      // independent fma chains of the head sum
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
+constexpr int kPfBinBits = 11;   // fused: top key bits of the running bound
+constexpr int kPfBins = 1 << kPfBinBits;
+// One pad word per 16 bins: a lane's 16 consecutive bins then sit in 16
+// different banks from every other lane's.
+constexpr int kPfHistWords = kPfBins + kPfBins / 16;
+__device__ __forceinline__ int pf_bin_at(uint32_t b) { return (int)(b + (b >> 4)); }
+
+// Outputs of the fused variant.
+struct PfFuseArgs {
+  int k;               // keys to select per row
+  uint32_t* key;       // candidate keys, Lmax per row, in position order
+  int32_t* pos;        // candidate positions, same layout
+  uint32_t* cnt;       // candidates per row
+};
+
+// Bin of the kk-th largest count of a wave's histogram (bins from the top),
+// or cur when it counts fewer than kk.  Lane l sums bins 16 (63 - l) ..
+// 16 (63 - l) + 15, so the lane prefix runs from the top bin down.
+__device__ uint32_t pf_wave_bound(const uint32_t* h, uint32_t kk, int lane, uint32_t cur) {
+  constexpr int PER = kPfBins / kWave;
+  const uint32_t lo = (uint32_t)(kWave - 1 - lane) * PER;  // lane 0: the top 16 bins
+  uint32_t c[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = h[pf_bin_at(lo + i)];
+    sum += c[i];
+  }
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint64_t m = __ballot(incl >= kk);
+  if (m == 0) return cur;
+  const int first = __builtin_ctzll(m);
+  uint32_t acc = incl - sum, bin = lo;
+  bool found = false;
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    acc += c[i];
+    if (!found && acc >= kk) {
+      bin = lo + i;
+      found = true;
+    }
+  }
+  return (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+}
 
 // fp8: at most 128 registers per lane so that two workgroups share a CU (four
 // waves per SIMD hide each other's MFMA and epilogue; measured 3% faster than
 // two waves even with a few spilled registers).  bf16 needs more registers
 // (its query block is twice the size) and keeps two waves per SIMD.
-template <bool FP8, int D, int HB>
-__global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kernel(
+template <bool FP8, int D, int HB, bool FUSE>
+__global__ __launch_bounds__(kPfThreads, (FP8 && !FUSE) ? 4 : 2) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
-    int Lmax, float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+    int Lmax, float* __restrict__ scores, int64_t ld, int keys_per_wg, PfFuseArgs fa) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int ROWB = D * EB;          // bytes per key row
   constexpr int PITCH = ROWB + 16;      // LDS row pitch
@@ -51,6 +108,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
   static_assert(CH >= 1 && kPfTile * CPR % kPfThreads == 0, "tile staging");
   __shared__ __align__(16) uint8_t ks[2][kPfTile * PITCH];
   __shared__ float kss[2][kPfTile];
+  __shared__ uint32_t whist[FUSE ? kPfWaves * kPfHistWords : 1];  // fused: per-wave histograms
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -69,11 +127,20 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
   const int k0 = blockIdx.y * keys_per_wg;
   const int k1 = min(Lmax, k0 + keys_per_wg);
   const int kc = (int)max((int64_t)k0, min((int64_t)k1, pos_max + 1));  // computed: [k0, kc)
-  float* srow = scores + row * ld;
+  float* srow = FUSE ? nullptr : scores + row * ld;
 
-  if (live)
+  if (!FUSE && live)
     for (int s = kc + lane; s < k1; s += kWave) srow[s] = -INFINITY;
-  if (kc <= k0) return;  // uniform over the workgroup
+  if (kc <= k0) {  // uniform over the workgroup
+    if (FUSE && live && lane == 0) fa.cnt[row] = 0;
+    return;
+  }
+  if constexpr (FUSE)
+    for (int i = tid; i < kPfWaves * kPfHistWords; i += kPfThreads) whist[i] = 0;
+  uint32_t* wh = whist + (FUSE ? wave * kPfHistWords : 0);
+  uint32_t* ckr = FUSE ? fa.key + row * Lmax : nullptr;
+  int32_t* cpr = FUSE ? fa.pos + row * Lmax : nullptr;
+  uint32_t wcount = 0, wbound = 0;  // fused: candidates so far, current bound
 
   // Query fragments and head weights (zero for padded heads; an idle wave
   // reads the last query row and stores nothing).
@@ -116,7 +183,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(FP8 ? k_scale + (int64_t)b * Lmax : k_scale), 0, FP8 ? Lmax * 4 : 0, kBufferWord3);
   const __amdgpu_buffer_rsrc_t outr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, Lmax * 4, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, FUSE ? 0 : Lmax * 4, kBufferWord3);
   const int ntiles = (kc - k0 + kPfTile - 1) / kPfTile;
 
   i32x4 stage[CH];
@@ -202,45 +269,65 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
         sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
       const int key = kbase + col;
-      if (g == 0 && live && key < kc) {
+      if constexpr (FUSE) {
+        const bool vis = g == 0 && live && key < kc && key <= pos;
+        const uint32_t kk = float_key(FP8 ? sc * kss[buf][sb * 32 + col] : sc);
+        const uint32_t bin = kk >> (32 - kPfBinBits);
+        if (vis) atomicAdd(&wh[pf_bin_at(bin)], 1u);
+        const bool cand = vis && bin >= wbound;
+        const uint64_t m = __ballot(cand);
+        if (cand) {
+          const uint32_t at =
+              wcount + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          ckr[at] = kk;
+          cpr[at] = key;
+        }
+        wcount += (uint32_t)__popcll(m);
+      } else if (g == 0 && live && key < kc) {
         const float o = key <= pos ? (FP8 ? sc * kss[buf][sb * 32 + col] : sc) : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, col * 4, kbase * 4, 0);
       }
     }
+    if constexpr (FUSE) {  // tighten the bound every 4 tiles (its own lanes' adds are done)
+      if ((tile & 3) == 3) wbound = pf_wave_bound(wh, (uint32_t)fa.k, lane, wbound);
+    }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
   }
+  if constexpr (FUSE) {
+    if (live && lane == 0) fa.cnt[row] = wcount;
+  }
 }
 
-template <bool FP8, int D, int HB>
+template <bool FP8, int D, int HB, bool FUSE>
 hipError_t launch_pf(const void* q, const float* q_scale, const float* w, const void* k,
                      const float* k_scale, const int32_t* ctx_len, int B, int T, int H, int Lmax,
-                     float* scores, int64_t ld, hipStream_t stream) {
+                     float* scores, int64_t ld, const PfFuseArgs& fa, hipStream_t stream) {
   const int qgroups = (T + kPfWaves - 1) / kPfWaves;
   const int tiles = (Lmax + kPfTile - 1) / kPfTile;
-  // Split the keys so the grid holds >= ~8 workgroups per CU.
+  // Split the keys so the grid holds >= ~8 workgroups per CU (the fused
+  // variant keeps each row in one workgroup).
   int splits = (2048 + qgroups * B - 1) / (qgroups * B);
   splits = max(splits, 8);
-  splits = max(1, min(splits, tiles));
+  splits = FUSE ? 1 : max(1, min(splits, tiles));
   const int tiles_per = (tiles + splits - 1) / splits;
   const int keys_per_wg = tiles_per * kPfTile;
   const dim3 grid(qgroups, (Lmax + keys_per_wg - 1) / keys_per_wg, B);
-  hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D, HB>), grid, dim3(kPfThreads), 0, stream,
-                     (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, ctx_len, T, H,
-                     Lmax, scores, ld, keys_per_wg);
+  hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D, HB, FUSE>), grid, dim3(kPfThreads), 0,
+                     stream, (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, ctx_len,
+                     T, H, Lmax, scores, ld, keys_per_wg, fa);
   return hipGetLastError();
 }
 
-}  // namespace
-
-bool indexer_prefill_supported(int H, int D) { return H >= 1 && H <= 64 && (D == 64 || D == 128); }
-
-hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale, const float* w,
-                                  const void* k, const float* k_scale, const int32_t* ctx_len,
-                                  int B, int T, int H, int D, int Lmax, float* scores,
-                                  int64_t ld, hipStream_t stream) {
-#define DSA_PF(F8, DD, HBB) \
-  return launch_pf<F8, DD, HBB>(q, q_scale, w, k, k_scale, ctx_len, B, T, H, Lmax, scores, ld, stream)
+template <bool FUSE>
+hipError_t dispatch_pf(const void* q, bool fp8, const float* q_scale, const float* w,
+                       const void* k, const float* k_scale, const int32_t* ctx_len, int B, int T,
+                       int H, int D, int Lmax, float* scores, int64_t ld, const PfFuseArgs& fa,
+                       hipStream_t stream) {
+#define DSA_PF(F8, DD, HBB)                                                                \
+  return launch_pf<F8, DD, HBB, FUSE>(q, q_scale, w, k, k_scale, ctx_len, B, T, H, Lmax, \
+                                      scores, ld, fa, stream)
   const bool two = H > 32;
   if (D == 128) {
     if (fp8) { if (two) DSA_PF(true, 128, 2); DSA_PF(true, 128, 1); }
@@ -251,6 +338,42 @@ hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale,
   if (two) DSA_PF(false, 64, 2);
   DSA_PF(false, 64, 1);
 #undef DSA_PF
+}
+
+}  // namespace
+
+bool indexer_prefill_supported(int H, int D) { return H >= 1 && H <= 64 && (D == 64 || D == 128); }
+
+hipError_t launch_indexer_prefill(const void* q, bool fp8, const float* q_scale, const float* w,
+                                  const void* k, const float* k_scale, const int32_t* ctx_len,
+                                  int B, int T, int H, int D, int Lmax, float* scores,
+                                  int64_t ld, hipStream_t stream) {
+  return dispatch_pf<false>(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax, scores,
+                            ld, PfFuseArgs{}, stream);
+}
+
+size_t indexer_topk_prefill_workspace_bytes(int B, int T, int Lmax) {
+  const size_t rows = (size_t)B * T;
+  auto a = [](size_t x) { return (x + 255) & ~size_t(255); };
+  return 2 * a(rows * (size_t)Lmax * 4) + a(rows * 4);
+}
+
+hipError_t launch_indexer_topk_prefill(const void* q, bool fp8, const float* q_scale,
+                                       const float* w, const void* k, const float* k_scale,
+                                       const int32_t* ctx_len, int B, int T, int H, int D,
+                                       int Lmax, int k_sel, int32_t* idx, void* workspace,
+                                       hipStream_t stream) {
+  const size_t rows = (size_t)B * T;
+  auto a = [](size_t x) { return (x + 255) & ~size_t(255); };
+  unsigned char* p = static_cast<unsigned char*>(workspace);
+  uint32_t* key = reinterpret_cast<uint32_t*>(p);
+  int32_t* pos = reinterpret_cast<int32_t*>(p + a(rows * (size_t)Lmax * 4));
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(p + 2 * a(rows * (size_t)Lmax * 4));
+  const PfFuseArgs fa{k_sel, key, pos, cnt};
+  hipError_t e = dispatch_pf<true>(q, fp8, q_scale, w, k, k_scale, ctx_len, B, T, H, D, Lmax,
+                                   nullptr, 0, fa, stream);
+  if (e != hipSuccess) return e;
+  return launch_topk_candidates(ctx_len, B, T, Lmax, k_sel, key, pos, cnt, idx, stream);
 }
 
 }  // namespace dsa

@@ -73,6 +73,23 @@ hipError_t launch_indexer_topk_decode(const void* q, bool fp8, const float* q_sc
                                       int Lmax, int k_sel, int32_t* idx, void* workspace,
                                       hipStream_t stream);
 
+// Prefill form of the fused indexer + top-k (T > 1, the prefill kernel's
+// shapes): each wave scores one query row over all its keys and appends the
+// scores in bins at or above its running bound to the row's candidate list;
+// launch_topk_candidates then selects per row.  Workspace: candidate keys
+// and positions (Lmax per row each), per-row counts; nothing to keep zero.
+size_t indexer_topk_prefill_workspace_bytes(int B, int T, int Lmax);
+hipError_t launch_indexer_topk_prefill(const void* q, bool fp8, const float* q_scale,
+                                       const float* w, const void* k, const float* k_scale,
+                                       const int32_t* ctx_len, int B, int T, int H, int D,
+                                       int Lmax, int k_sel, int32_t* idx, void* workspace,
+                                       hipStream_t stream);
+// Per-row top-k among position-ordered candidate lists (key, position) of
+// cnt[row] entries at row * Lmax, which hold every key of the row's top k.
+hipError_t launch_topk_candidates(const int32_t* ctx_len, int B, int T, int Lmax, int k,
+                                  const uint32_t* key, const int32_t* pos, const uint32_t* cnt,
+                                  int32_t* idx, hipStream_t stream);
+
 size_t sparse_attn_workspace_bytes(int B, int T, int Hq, int k, int d_v);
 hipError_t launch_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                               const int32_t* ctx_len, int B, int T, int Hq, int Lmax, int k,

@@ -580,6 +580,72 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   finish_from_list((int)listed, b1, above1, k, out, sm);
 }
 
+// Top-k per row among a position-ordered candidate list that holds every
+// key of the row's top k (the fused prefill indexer's output): the list is
+// copied into LDS (kGather entries per thread in flight) while its first
+// radix digit is counted, then steps 3-4 run on it; the extra candidates
+// below the threshold are never emitted.  A list longer than the LDS list is
+// finished from memory.
+__global__ __launch_bounds__(kTkThreads) void topk_cand_kernel(
+    const int32_t* __restrict__ ctx_len, int T, int Lmax, int k,
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
+    const uint32_t* __restrict__ cand_cnt, int32_t* __restrict__ idx) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int n = visible(ctx_len, row, T, Lmax);
+  int32_t* out = idx + (int64_t)row * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int M = (int)cand_cnt[row];  // >= k: the row's top k are all listed
+  const uint32_t* ck = cand_key + (int64_t)row * Lmax;
+  const int32_t* cp = cand_pos + (int64_t)row * Lmax;
+  for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  const bool fits = M <= kTkCap;
+  if (fits) {
+    for (int e0 = tid; e0 < M; e0 += kGather * kTkThreads) {
+      uint32_t kv[kGather];
+      int32_t pv[kGather];
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) {
+        const int e = min(e0 + u * kTkThreads, M - 1);
+        kv[u] = ck[e];
+        pv[u] = cp[e];
+      }
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) {
+        const int e = e0 + u * kTkThreads;
+        if (e < M) {
+          sm.list_key[e] = kv[u];
+          sm.list_pos[e] = pv[u];
+          atomicAdd(&sm.hist[kv[u] >> 20], 1u);
+        }
+      }
+    }
+  } else {
+    for (int e = tid; e < M; e += kTkThreads) atomicAdd(&sm.hist[ck[e] >> 20], 1u);
+  }
+  __syncthreads();
+  select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
+  const uint32_t b1 = sm.sel[0];
+  const uint32_t above1 = sm.sel[1];
+  __syncthreads();
+  if (fits) {
+    finish_from_list(M, b1, above1, k, out, sm);
+    return;
+  }
+  if (tid == 0) {
+    sm.chunk_off[0] = 0;
+    sm.chunk_off[1] = (uint32_t)M;
+  }
+  __syncthreads();
+  finish_from_slices(ck, cp, Lmax, 1, M, b1, above1, k, out, sm);
+}
+
 struct TopkPlan {
   bool chunked;
   int chunk, n_chunks;
@@ -673,6 +739,17 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* ctx_len, 
   if (e != hipSuccess) return e;
   return launch_topk_finish(scores, ld, ctx_len, B, T, Lmax, k, p.chunk, p.n_chunks, w, false,
                             idx, stream);
+}
+
+hipError_t launch_topk_candidates(const int32_t* ctx_len, int B, int T, int Lmax, int k,
+                                  const uint32_t* key, const int32_t* pos, const uint32_t* cnt,
+                                  int32_t* idx, hipStream_t stream) {
+  const size_t smem = sizeof(TopkSmem);
+  hipError_t e = set_smem_attr((const void*)topk_cand_kernel, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_cand_kernel, dim3(B * T), dim3(kTkThreads), smem, stream, ctx_len, T,
+                     Lmax, k, key, pos, cnt, idx);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_finish(const float* scores, int64_t ld, const int32_t* ctx_len, int B,

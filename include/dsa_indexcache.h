@@ -107,26 +107,30 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, const int32_t* ctx
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Indexer scores and top-k in one pass for one-query-row (decode) shapes
- * (technical summary §1: the indexer scores every previous token and keeps
- * the k most relevant; the scores are consumed only by that selection).
- * idx [B,T,k_sel] is exactly what dsa_indexer_scores followed by dsa_topk
- * write for the same inputs (the same fp32 scores decide the same
- * selection), but the scores never reach memory: each workgroup keeps its
- * keys' scores in LDS and compacts its own candidates against a lower bound
- * of the row's threshold (taken from the row histogram in the workspace as
- * it stands, no workgroup waiting for another), then one workgroup per row
- * completes the selection from the finished histogram.
- * Arguments are those of dsa_indexer_scores and dsa_topk (k_sel is dsa_topk's
- * k), with the same limits.
- * Supported where the one-query-row indexer kernel runs (T == 1, or H / D
- * that the prefill kernel does not take) and a row splits into at most 1024
- * workgroups (Lmax up to 8388608 fp8 keys at D = 128);
- * dsa_indexer_topk_workspace_size returns DSA_ERR_UNSUPPORTED otherwise.
- * workspace: dsa_indexer_topk_workspace_size bytes (device), zero-filled
- * before its first use; every call leaves its leading histograms zero
- * again.  Its layout is dsa_topk's, so one zero-filled buffer of the larger
- * size serves both.  Calls sharing a workspace must not run concurrently.
+ * Indexer scores and top-k in one pass (technical summary §1: the indexer
+ * scores every previous token and keeps the k most relevant; the scores are
+ * consumed only by that selection).  idx [B,T,k_sel] is exactly what
+ * dsa_indexer_scores followed by dsa_topk write for the same inputs (the
+ * same fp32 scores decide the same selection), but the scores never reach
+ * memory.  Arguments are those of dsa_indexer_scores and dsa_topk (k_sel is
+ * dsa_topk's k), with the same limits.
+ *   One query row per sequence (decode): each workgroup keeps its keys'
+ *   scores in LDS and compacts its own candidates against a lower bound of
+ *   the row's threshold (the row histogram in the workspace as it stands;
+ *   no workgroup waits for another), then one workgroup per row completes
+ *   the selection from the finished histogram.  A row may split into at
+ *   most 1024 workgroups (Lmax up to 8388608 fp8 keys at D = 128);
+ *   dsa_indexer_topk_workspace_size returns DSA_ERR_UNSUPPORTED beyond.
+ *   Workspace: zero-filled before its first use; every call leaves its
+ *   leading histograms zero again (dsa_topk's layout, so one zero-filled
+ *   buffer of the larger size serves both).
+ *   Several query rows per sequence (prefill, the shapes the prefill
+ *   indexer takes): each wave scores one row over all its keys and appends
+ *   the scores at or above its running bound (the threshold bin of the keys
+ *   seen so far) to the row's candidate list, then one workgroup per row
+ *   selects among the candidates.  Workspace: 8 bytes per key and row plus
+ *   4 per row; no state kept between calls.
+ * Calls sharing a workspace must not run concurrently.
  */
 dsa_status_t dsa_indexer_topk_workspace_size(int B, int T, int H, int D, dsa_dtype_t dtype,
                                              int Lmax, int k_sel, size_t* bytes);
@@ -239,10 +243,10 @@ typedef struct dsa_stack_stats {
  * nothing to inherit and is rejected).  For layer l:
  *   'F': scores = dsa_indexer_scores(layer l) into score_buf, then
  *        dsa_topk into idx_buf              (the index cache is written);
- *        where dsa_indexer_topk takes the shape and flags does not hold
+ *        for decode shapes that dsa_indexer_topk takes, unless flags holds
  *        DSA_STACK_UNFUSED_TOPK, dsa_indexer_topk into idx_buf instead
  *        (the same set; score_buf is then neither written nor needed and
- *        may be NULL)
+ *        may be NULL; see indexcache_stack_fuses_topk)
  *   'S': nothing                            (idx_buf is reused in place)
  *   then, if Hq > 0, dsa_sparse_attn(layer l, idx_buf).
  * idx_buf [B,T,k] int32 holds the last F layer's set when the call returns.
@@ -254,6 +258,10 @@ typedef struct dsa_stack_stats {
  * number of kernels of each kind that were enqueued.
  */
 dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* shape, size_t* bytes);
+/* *fused = 1 when indexcache_run_stack runs F layers of this shape through
+ * dsa_indexer_topk (decode shapes it takes, flags without
+ * DSA_STACK_UNFUSED_TOPK; score_buf may then be NULL), else 0. */
+dsa_status_t indexcache_stack_fuses_topk(const dsa_stack_shape_t* shape, int* fused);
 dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_layer_t* layers,
                                   const dsa_stack_shape_t* shape, const int32_t* ctx_len,
                                   int32_t* idx_buf, float* score_buf, int64_t ld_scores,

@@ -238,10 +238,21 @@ def test_fused_indexer_topk_host_checks(lib):
     assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 8388608, 2048, ctypes.byref(need)) == 0
     assert ws(1, 1, 64, 128, _lib.DSA_FP8_E4M3, 8388608 + 64, 2048,
               ctypes.byref(need)) == _lib.DSA_ERR_UNSUPPORTED
-    # several query rows per sequence run the prefill indexer: not fused
-    assert ws(1, 16, 64, 128, _lib.DSA_FP8_E4M3, 8192, 2048,
-              ctypes.byref(need)) == _lib.DSA_ERR_UNSUPPORTED
-    assert "prefill" in _err(lib)
+    # several query rows per sequence: the prefill form, candidate lists of
+    # Lmax keys and positions per row plus a count per row
+    assert ws(1, 16, 64, 128, _lib.DSA_FP8_E4M3, 8192, 2048, ctypes.byref(need)) == 0
+    assert need.value == 2 * a(16 * 8192 * 4) + a(16 * 4)
+    # the stack fuses decode shapes only, unless told not to
+    fz = ctypes.c_int(-1)
+    dec = _lib.StackShape(8, 1, 64, 128, 131072, 2048, 0, 576, 512, _lib.DSA_FP8_E4M3, 0.1)
+    assert lib.indexcache_stack_fuses_topk(ctypes.byref(dec), ctypes.byref(fz)) == 0
+    assert fz.value == 1
+    dec.flags = _lib.DSA_STACK_UNFUSED_TOPK
+    assert lib.indexcache_stack_fuses_topk(ctypes.byref(dec), ctypes.byref(fz)) == 0
+    assert fz.value == 0
+    pre = _lib.StackShape(1, 8192, 64, 128, 65536, 2048, 0, 576, 512, _lib.DSA_FP8_E4M3, 0.1)
+    assert lib.indexcache_stack_fuses_topk(ctypes.byref(pre), ctypes.byref(fz)) == 0
+    assert fz.value == 0
     f = lib.dsa_indexer_topk
     # fp8 without scales; NULL output; workspace too small
     assert f(16, _lib.DSA_FP8_E4M3, None, 16, 16, None, 16, 1, 1, 64, 128, 4096, 64, 16, 16,

@@ -33,8 +33,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def make_case(B, H, D, Lmax, dtype, seed, keys="random"):
-    s = gen.Shape(seed, "fused", 1, "F", B=B, T=1, ctx=Lmax, H=H, D=D, idx_dtype=dtype, k=1)
+def make_case(B, H, D, Lmax, dtype, seed, keys="random", T=1):
+    s = gen.Shape(seed, "fused", 1, "F", B=B, T=T, ctx=Lmax, H=H, D=D, idx_dtype=dtype, k=1)
     qi = gen.make_indexer_query(s, DEV, w_low=-0.3)
     ki = gen.make_indexer_keys(s, 1, gen.make_key_base(s, DEV), DEV)
     k, ks = ki.k, ki.k_scale
@@ -121,9 +121,49 @@ def test_fused_workspace_reuse():
         assert _zero_region(ws, B), f"seed {seed}: workspace not left zero"
 
 
-def test_fused_rejects_prefill_shapes():
-    with pytest.raises(dsa.DSAError):
-        dsa.indexer_topk_workspace_size(1, 64, 64, 128, 4096, 2048, "fp8")
+PREFILL_CASES = [
+    # B, T, H, D, Lmax, ctx, k, dtype, keys
+    (2, 5, 64, 128, 1030, [1030, 517], 256, "fp8", "random"),
+    (1, 64, 64, 128, 2080, [2080], 512, "bf16", "random"),
+    (1, 300, 64, 128, 5000, [5000], 1024, "fp8", "random"),     # T not a multiple of 8
+    (2, 17, 64, 64, 900, [900, 500], 128, "bf16", "random"),     # D = 64, ragged ctx
+    (1, 40, 20, 128, 4000, [3000], 256, "bf16", "random"),       # ctx < Lmax, H < 32
+    (1, 16, 64, 128, 40000, [40000], 2048, "fp8", "equal"),      # every key listed: past LDS
+    (1, 24, 64, 128, 30000, [30000], 2048, "bf16", "few"),       # heavy ties
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES,
+                         ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}D{c[3]}L{c[4]}k{c[6]}{c[7]}-{c[8]}")
+def test_fused_prefill_equals_oracle_selection(case):
+    """Prefill form (several query rows per sequence, running bound per row,
+    candidate lists): exactly the oracle's top-k over the GPU's fp32 scores,
+    and the separate kernels' selection."""
+    B, T, H, D, Lmax, ctx, k, dtype, keys = case
+    say("fused prefill indexer + top-k case", case)
+    qi, kc, ks = make_case(B, H, D, Lmax, dtype, seed=60 + T + D, keys=keys, T=T)
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    got = dsa.indexer_topk(qi.q, qi.w, kc, ctx_t, k, qi.q_scale, ks)
+    sc = dsa.indexer_scores(qi.q, qi.w, kc, ctx_t, qi.q_scale, ks)
+    sep = dsa.topk(sc, ctx_t, k)
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    parity.check_topk_exact(g, sc.cpu().numpy(), ctx, k)
+    assert np.array_equal(g, sep.cpu().numpy())
+
+
+def test_fused_prefill_chunk_equals_separate():
+    """The 8192-query prefill chunk on a 65536-token context: the fused form's
+    sets equal the separate kernels' for every row (the separate path is held
+    to the oracle at this size by the full-size parity tests)."""
+    B, T, H, D, L, k = 1, 8192, 64, 128, 65536, 2048
+    qi, kc, ks = make_case(B, H, D, L, "fp8", seed=70, T=T)
+    ctx_t = torch.tensor([L], dtype=torch.int32, device=DEV)
+    got = dsa.indexer_topk(qi.q, qi.w, kc, ctx_t, k, qi.q_scale, ks)
+    sc = dsa.indexer_scores(qi.q, qi.w, kc, ctx_t, qi.q_scale, ks)
+    sep = dsa.topk(sc, ctx_t, k)
+    torch.cuda.synchronize()
+    assert torch.equal(got, sep)
 
 
 @pytest.mark.parametrize("idx_dtype,D", [("fp8", 128), ("bf16", 64)])
