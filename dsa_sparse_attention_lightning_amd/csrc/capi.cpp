@@ -185,7 +185,7 @@ bool stack_fuses_topk(const dsa_stack_shape_t* s) {
 }
 
 // Room for the separate top-k's workspace and for the fused path's (both
-// start with the same zero-kept histograms and arrival words).
+// start with the same zero-kept histograms).
 size_t topk_region(const dsa_stack_shape_t* s) {
   size_t b = dsa::topk_workspace_bytes(s->B, s->T, s->Lmax, s->k);
   if (!uses_prefill_indexer(s->T, s->H, s->D) &&
