@@ -21,16 +21,17 @@
 //
 // Fused variant (FUSE, feeding the top-k without writing scores): a
 // workgroup takes its 8 query rows over all their keys, so each wave owns
-// one row.  The wave counts its visible scores' top 11 key bits in its own
-// LDS histogram (one workgroup per CU, two waves per SIMD: the eight 8.5 KB
-// histograms and the key tiles fill 105 KB) and, every 4 tiles, takes the
-// bin holding the k-th largest
+// one row.  The wave counts its visible scores' top 10 key bits in its own
+// LDS histogram and, every 4 tiles, takes the bin holding the k-th largest
 // count so far as its row's bound: the k-th largest of the keys seen so far
 // is at most the row's, so every key of the row's top k lies in a bin at or
-// above any bound taken on the way.  Scores in bins at or above the current
-// bound are appended, in position order, to the row's candidate list (a
-// wave-wide ballot gives each its slot); a per-row kernel then selects the
-// top k among the candidates.
+// above any bound taken on the way.  Inside the bound's bin the wave also
+// counts the next 6 key bits (restarted whenever the bound moves to a higher
+// bin, so it can only undercount) and takes a sub-bin bound the same way.
+// Scores at or above the current bound are appended, in position order, to
+// the row's candidate list (a wave-wide ballot gives each its slot); a
+// per-row kernel then selects the top k among the candidates.  The eight
+// histograms and the key tiles take 75 KB, so two workgroups share a CU.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -43,11 +44,13 @@ constexpr int kPfTile = 128;   // keys per LDS tile
 constexpr int kParts = 4;      // independent fma chains of the head sum
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
-constexpr int kPfBinBits = 11;   // fused: top key bits of the running bound
+constexpr int kPfBinBits = 10;   // fused: top key bits of the running bound
 constexpr int kPfBins = 1 << kPfBinBits;
+constexpr int kPfSubBits = 6;    // fused: next key bits, counted inside the bound's bin
+constexpr int kPfSubs = 1 << kPfSubBits;
 // One pad word per 16 bins: a lane's 16 consecutive bins then sit in 16
 // different banks from every other lane's.
-constexpr int kPfHistWords = kPfBins + kPfBins / 16;
+constexpr int kPfHistWords = kPfBins + kPfBins / 16 + kPfSubs;  // + the sub-histogram
 __device__ __forceinline__ int pf_bin_at(uint32_t b) { return (int)(b + (b >> 4)); }
 
 // Outputs of the fused variant.
@@ -61,9 +64,10 @@ struct PfFuseArgs {
 // Bin of the kk-th largest count of a wave's histogram (bins from the top),
 // or cur when it counts fewer than kk.  Lane l sums bins 16 (63 - l) ..
 // 16 (63 - l) + 15, so the lane prefix runs from the top bin down.
-__device__ uint32_t pf_wave_bound(const uint32_t* h, uint32_t kk, int lane, uint32_t cur) {
+__device__ uint32_t pf_wave_bound(const uint32_t* h, uint32_t kk, int lane, uint32_t cur,
+                                  uint32_t& above) {
   constexpr int PER = kPfBins / kWave;
-  const uint32_t lo = (uint32_t)(kWave - 1 - lane) * PER;  // lane 0: the top 16 bins
+  const uint32_t lo = (uint32_t)(kWave - 1 - lane) * PER;  // lane 0: the top PER bins
   uint32_t c[PER];
   uint32_t sum = 0;
 #pragma unroll
@@ -75,17 +79,27 @@ __device__ uint32_t pf_wave_bound(const uint32_t* h, uint32_t kk, int lane, uint
   const uint64_t m = __ballot(incl >= kk);
   if (m == 0) return cur;
   const int first = __builtin_ctzll(m);
-  uint32_t acc = incl - sum, bin = lo;
+  uint32_t acc = incl - sum, bin = lo, abv = 0;
   bool found = false;
 #pragma unroll
   for (int i = PER - 1; i >= 0; --i) {
-    acc += c[i];
-    if (!found && acc >= kk) {
+    if (!found && acc + c[i] >= kk) {
       bin = lo + i;
+      abv = acc;
       found = true;
     }
+    acc += c[i];
   }
+  above = (uint32_t)__builtin_amdgcn_readlane((int)abv, first);
   return (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+}
+
+// Sub-bin bound inside the bound's bin: the highest sub-bin s with at least
+// need counts in sub-bins >= s (lane l holds sub-bin 63 - l), or 0.
+__device__ uint32_t pf_sub_bound(const uint32_t* sh, uint32_t need, int lane) {
+  const uint32_t incl = wave_incl_scan(sh[kPfSubs - 1 - lane]);
+  const uint64_t m = __ballot(incl >= need);
+  return m == 0 ? 0u : (uint32_t)(kPfSubs - 1 - __builtin_ctzll(m));
 }
 
 // fp8: at most 128 registers per lane so that two workgroups share a CU (four
@@ -93,7 +107,7 @@ __device__ uint32_t pf_wave_bound(const uint32_t* h, uint32_t kk, int lane, uint
 // two waves even with a few spilled registers).  bf16 needs more registers
 // (its query block is twice the size) and keeps two waves per SIMD.
 template <bool FP8, int D, int HB, bool FUSE>
-__global__ __launch_bounds__(kPfThreads, (FP8 && !FUSE) ? 4 : 2) void indexer_prefill_kernel(
+__global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
@@ -140,7 +154,8 @@ __global__ __launch_bounds__(kPfThreads, (FP8 && !FUSE) ? 4 : 2) void indexer_pr
   uint32_t* wh = whist + (FUSE ? wave * kPfHistWords : 0);
   uint32_t* ckr = FUSE ? fa.key + row * Lmax : nullptr;
   int32_t* cpr = FUSE ? fa.pos + row * Lmax : nullptr;
-  uint32_t wcount = 0, wbound = 0;  // fused: candidates so far, current bound
+  uint32_t* wsh = wh + kPfBins + kPfBins / 16;  // fused: sub-histogram of the bound's bin
+  uint32_t wcount = 0, wbound = 0, wsub = 0;  // fused: candidates, bound bin and sub-bin
 
   // Query fragments and head weights (zero for padded heads; an idle wave
   // reads the last query row and stores nothing).
@@ -273,8 +288,10 @@ __global__ __launch_bounds__(kPfThreads, (FP8 && !FUSE) ? 4 : 2) void indexer_pr
         const bool vis = g == 0 && live && key < kc && key <= pos;
         const uint32_t kk = float_key(FP8 ? sc * kss[buf][sb * 32 + col] : sc);
         const uint32_t bin = kk >> (32 - kPfBinBits);
+        const uint32_t sub = (kk >> (32 - kPfBinBits - kPfSubBits)) & (kPfSubs - 1);
         if (vis) atomicAdd(&wh[pf_bin_at(bin)], 1u);
-        const bool cand = vis && bin >= wbound;
+        if (vis && bin == wbound) atomicAdd(&wsh[sub], 1u);
+        const bool cand = vis && (bin > wbound || (bin == wbound && sub >= wsub));
         const uint64_t m = __ballot(cand);
         if (cand) {
           const uint32_t at =
@@ -290,7 +307,19 @@ __global__ __launch_bounds__(kPfThreads, (FP8 && !FUSE) ? 4 : 2) void indexer_pr
       }
     }
     if constexpr (FUSE) {  // tighten the bound every 4 tiles (its own lanes' adds are done)
-      if ((tile & 3) == 3) wbound = pf_wave_bound(wh, (uint32_t)fa.k, lane, wbound);
+      if ((tile & 3) == 3) {
+        uint32_t above = 0;
+        const uint32_t nb = pf_wave_bound(wh, (uint32_t)fa.k, lane, wbound, above);
+        if (nb != wbound) {  // a higher bin: its earlier keys were not sub-counted, restart
+          wbound = nb;
+          wsub = 0;
+          wsh[lane] = 0;
+        } else if (nb > 0 || above > 0) {
+          // the sub-histogram undercounts the bin (keys before it became the
+          // bound), which can only lower the sub-bound: still a lower bound
+          wsub = pf_sub_bound(wsh, (uint32_t)fa.k - above, lane);
+        }
+      }
     }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
