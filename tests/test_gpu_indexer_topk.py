@@ -103,21 +103,27 @@ def _zero_region(ws, rows):
 
 
 def test_fused_workspace_reuse():
-    """One workspace across calls (different queries, ragged rows including
-    n <= k): every result equals the separate path's and the part of the
-    workspace that must start at zero is zero after every call."""
+    """One workspace across many calls (different queries, ragged rows
+    including n <= k), the separate top-k using the same workspace in
+    between: every result equals the separate path's, and the part of the
+    workspace that must start at zero is zero after every call.  (A read of
+    the row histogram that saw a previous call's counts would raise the
+    bound above the true one and drop selected keys.)"""
     B, H, D, L, k = 3, 64, 128, 65536, 2048
     ctx = [65536, 40000, 2000]
     ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
-    nbytes = dsa.indexer_topk_workspace_size(B, 1, H, D, L, k, "fp8")
+    nbytes = max(dsa.indexer_topk_workspace_size(B, 1, H, D, L, k, "fp8"),
+                 dsa.topk_workspace_size(B, 1, L, k))
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-    for seed in (1, 2, 3):
+    for seed in range(1, 9):
         qi, kc, ks = make_case(B, H, D, L, "fp8", seed=seed)
         got = dsa.indexer_topk(qi.q, qi.w, kc, ctx_t, k, qi.q_scale, ks, workspace=ws)
         sc = dsa.indexer_scores(qi.q, qi.w, kc, ctx_t, qi.q_scale, ks)
-        sep = dsa.topk(sc, ctx_t, k)
+        sep = dsa.topk(sc, ctx_t, k, workspace=ws)
+        again = dsa.indexer_topk(qi.q, qi.w, kc, ctx_t, k, qi.q_scale, ks, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(got, sep), f"seed {seed}"
+        assert torch.equal(again, sep), f"seed {seed}, after the separate top-k"
         assert _zero_region(ws, B), f"seed {seed}: workspace not left zero"
 
 
