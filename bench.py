@@ -279,6 +279,20 @@ def decode_bench(args, dev):
     return s, layers, res, cut, kernels, roof
 
 
+def reuse_overlap(own, reused) -> float:
+    """Share of one row's own selection (the set its layer's indexer and
+    top-k pick) that the reused set of the nearest F layer also holds:
+    |own ∩ reused| / |own|, -1 padding ignored (nan when own is empty).
+    Checked against the oracle's pinned overlap_fraction by the CPU tests."""
+    import numpy as np
+    a = np.asarray(own).reshape(-1)
+    b = np.asarray(reused).reshape(-1)
+    a = np.unique(a[a >= 0])
+    if a.size == 0:
+        return math.nan
+    return float(np.isin(a, b[b >= 0]).sum()) / a.size
+
+
 def pattern_sweep(dev, steps, warmup, cfg=4):
     """The pattern sweep near maximum context: step time, indexer+top-k time
     per layer, and the overlap between the index set each S layer reuses and
@@ -308,15 +322,14 @@ def pattern_sweep(dev, steps, warmup, cfg=4):
                 last_f = l
                 continue
             for b in range(s.B):
-                a, o = own[last_f][b, 0], own[l][b, 0]
-                ovs.append(np.intersect1d(a[a >= 0], o[o >= 0]).size / max(1, (o >= 0).sum()))
+                ovs.append(reuse_overlap(own[l][b, 0], own[last_f][b, 0]))
         key = "all-F" if set(p) == {"F"} else next(
             p[:n] for n in range(1, len(p) + 1) if gen.tile_pattern(p[:n], len(p)) == p)
         out[key] = dict(ms_per_step=round(ms, 4), tokens_per_s=round(s.B / (ms * 1e-3), 1),
                         n_indexer_calls=stats["n_indexer_calls"],
                         indexer_topk_us_per_layer=round(ms_i * 1e3 / s.n_layers, 3),
                         per_token_latency_ms=round(ms, 4),
-                        reuse_overlap=round(float(np.mean(ovs)), 4) if ovs else None)
+                        reuse_overlap=round(float(np.nanmean(ovs)), 4) if ovs else None)
         log(f"sweep {key:9s} {ms:7.3f} ms/step  indexer+topk {ms_i * 1e3 / s.n_layers:7.2f} "
             f"us/layer  overlap {out[key]['reuse_overlap']}")
     del layers

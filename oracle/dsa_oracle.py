@@ -50,6 +50,10 @@ Attention via Cross-Layer Index Reuse", gist.science es/pt/it/de editions):
   of its own selected positions missing from the reused set ("miss").  The
   layers of the synthetic stack take independent inputs, so this sum is the
   whole-stack difference against all-F, layer by layer.
+* overlap_fraction - the measured statistic the pages quote for adjacent
+  layers (technical summary §1 on the pt/it/de editions: their top-k
+  selections share 70% to 100% of tokens): the share of one row's own
+  selection that another layer's set for the same row also holds.
 * run_stack       - the IndexCache layer loop: F layers run the indexer and
   top-k and store the index set; S layers skip both and reuse the set of the
   nearest preceding F layer (technical summary §2, "Arquitectura del Método" /
@@ -419,9 +423,22 @@ def run_stack(pattern: str, layers: List[Dict[str, np.ndarray]], ctx_len: Sequen
 
 
 def overlap_fraction(a: np.ndarray, b: np.ndarray) -> float:
-    """|A ∩ B| / |A| for two index sets (the -1 padding is ignored)."""
-    sa = set(int(x) for x in np.asarray(a).ravel() if x >= 0)
-    sb = set(int(x) for x in np.asarray(b).ravel() if x >= 0)
+    """Share of one query row's index set A that another layer's set B for the
+    same row also holds: |A ∩ B| / |A|, the -1 padding of either set ignored
+    (nan when A selects nothing).  The pages report how far the top-k
+    selections of adjacent layers coincide (technical summary §1 on the
+    pt/it/de editions: 70% to 100%); with A the set a layer's own indexer
+    would select and B the set it reuses, this is the share of its own
+    selection that reuse keeps.  a and b hold one row each (leading size-1
+    dimensions are allowed): positions of different rows are not comparable."""
+    rows = []
+    for x in (a, b):
+        x = np.asarray(x)
+        if x.ndim == 0 or any(d != 1 for d in x.shape[:-1]):
+            raise ValueError("overlap_fraction takes one row's index set per argument")
+        rows.append(x.reshape(-1))
+    sa = set(int(x) for x in rows[0] if x >= 0)
+    sb = set(int(x) for x in rows[1] if x >= 0)
     if not sa:
         return math.nan
     return len(sa & sb) / len(sa)

@@ -533,6 +533,60 @@ def pin_search_identical_keys(o):
         assert [p for p, _ in trace] == ["FSFFF", "FSSFF", "FSSSF", "FSSSS"]
 
 
+# ---------------------------------------------------------------- overlap
+
+def pin_overlap_hand_worked(o):
+    """A = {3, 7, 9}, B = {1, 3, 9, 11}, both padded with -1: A and B share
+    {3, 9}, so 2 of A's 3 positions are kept (2/3) and 2 of B's 4 (1/2).
+    A set with nothing selected has no overlap to report (nan); an empty B
+    keeps nothing (0); a set against itself keeps everything (1)."""
+    a = np.array([3, 7, 9, -1, -1], dtype=np.int32)
+    b = np.array([1, 3, 9, 11, -1], dtype=np.int32)
+    assert abs(o.overlap_fraction(a, b) - 2 / 3) < 1e-15
+    assert abs(o.overlap_fraction(b, a) - 1 / 2) < 1e-15
+    assert abs(o.overlap_fraction(a[None, :], b[None, None, :]) - 2 / 3) < 1e-15
+    none = np.full(5, -1, dtype=np.int32)
+    assert math.isnan(o.overlap_fraction(none, b))
+    assert o.overlap_fraction(a, none) == 0.0
+    assert o.overlap_fraction(a, a) == 1.0
+    assert o.overlap_fraction(np.array([5, -1]), np.array([-1, 6])) == 0.0
+    try:
+        o.overlap_fraction(np.stack([a, a]), np.stack([b, b]))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("two rows at once must be rejected")
+
+
+def pin_overlap_bruteforce(o):
+    """Random ascending, -1-padded selections (as the top-k emits them):
+    count A's valid entries found anywhere among B's valid entries by
+    scanning, one entry at a time."""
+    r = RNG(31)
+    for _ in range(200):
+        k = int(r.integers(1, 12))
+        L = int(r.integers(k, 40))
+        sets = []
+        for _ in range(2):
+            n = int(r.integers(0, k + 1))
+            x = np.full(k, -1, dtype=np.int32)
+            x[:n] = np.sort(r.choice(L, size=n, replace=False))
+            sets.append(x)
+        a, b = sets
+        valid_a = [int(x) for x in a if x != -1]
+        found = 0
+        for x in valid_a:
+            for y in b:
+                if y != -1 and int(y) == x:
+                    found += 1
+                    break
+        got = o.overlap_fraction(a, b)
+        if not valid_a:
+            assert math.isnan(got)
+        else:
+            assert got == found / len(valid_a), (a, b, got)
+
+
 ALL_PINS = [
     pin_e4m3_table, pin_e4m3_values, pin_bf16_table,
     pin_indexer_closed_form, pin_indexer_bruteforce, pin_indexer_library,
@@ -545,4 +599,5 @@ ALL_PINS = [
     pin_bf16_encode_library, pin_fp8_row_quantisation, pin_kv_append,
     pin_search_cost_decomposition, pin_search_hand_trace, pin_search_row_constant,
     pin_search_bruteforce, pin_search_identical_keys,
+    pin_overlap_hand_worked, pin_overlap_bruteforce,
 ]

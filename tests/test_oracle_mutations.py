@@ -212,6 +212,17 @@ def _reuse_costs_variant(o, unnormalised=False, transposed=False):
     return f
 
 
+def _overlap(o, denom="a", count_padding=False):
+    def f(a, b):
+        a, b = np.asarray(a).reshape(-1), np.asarray(b).reshape(-1)
+        keep = (lambda x: True) if count_padding else (lambda x: x >= 0)
+        sa = set(int(x) for x in a if keep(x))
+        sb = set(int(x) for x in b if keep(x))
+        n = {"a": len(sa), "b": len(sb), "union": len(sa | sb)}[denom]
+        return math.nan if n == 0 else len(sa & sb) / n
+    return f
+
+
 MUTANTS = {
     "indexer_no_relu": ("indexer_scores_row", lambda o: _indexer_row(relu=False)),
     "indexer_w_inside_relu": ("indexer_scores_row", lambda o: _indexer_row(w_inside=True)),
@@ -238,6 +249,9 @@ MUTANTS = {
     "search_source_is_previous_layer": ("pattern_sources", _sources_previous_layer),
     "search_cost_unnormalised": ("reuse_costs", lambda o: _reuse_costs_variant(o, unnormalised=True)),
     "search_cost_transposed": ("reuse_costs", lambda o: _reuse_costs_variant(o, transposed=True)),
+    "overlap_divides_by_reused_set": ("overlap_fraction", lambda o: _overlap(o, denom="b")),
+    "overlap_counts_padding": ("overlap_fraction", lambda o: _overlap(o, count_padding=True)),
+    "overlap_is_jaccard": ("overlap_fraction", lambda o: _overlap(o, denom="union")),
 }
 
 
