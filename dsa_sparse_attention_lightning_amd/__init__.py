@@ -61,6 +61,64 @@ def _need(t, name, dtypes, ndim=None):
         raise TypeError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise TypeError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _same_device(ref, *named):
+    for name, t in named:
+        if t is not None and t.device != ref.device:
+            raise TypeError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _ctx(ctx_len, B):
+    _need(ctx_len, "ctx_len", (_torch().int32,), 1)
+    if ctx_len.shape[0] != B:
+        raise TypeError(f"ctx_len has {ctx_len.shape[0]} entries, expected B = {B}")
+
+
+def _workspace(ws, need: int, device, zero: bool):
+    """The caller's workspace (checked: contiguous uint8 on `device`; its real
+    size goes to the C ABI, which rejects one that is too small), or a fresh
+    one of `need` bytes."""
+    torch = _torch()
+    if ws is None:
+        alloc = torch.zeros if zero else torch.empty
+        return alloc(max(need, 1), dtype=torch.uint8, device=device)
+    _need(ws, "workspace", (torch.uint8,))
+    if ws.device != torch.device(device):
+        raise TypeError(f"workspace is on {ws.device}, expected {device}")
+    return ws
+
+
+def _indexer_inputs(q, w, k, ctx_len, q_scale, k_scale):
+    """Shapes of the indexer operands: q [B,T,H,D], w [B,T,H] fp32, k
+    [B,Lmax,D] of q's dtype, and for fp8 q_scale [B,T,H] and k_scale [B,Lmax]
+    fp32; ctx_len [B] int32."""
+    torch = _torch()
+    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), 4)
+    _need(k, "k", (q.dtype,), 3)
+    _need(w, "w", (torch.float32,), 3)
+    B, T, H, D = q.shape
+    Lmax = k.shape[1]
+    _shape(k, "k", (B, Lmax, D))
+    _shape(w, "w", (B, T, H))
+    _ctx(ctx_len, B)
+    if q.dtype == torch.float8_e4m3fn:
+        if q_scale is None or k_scale is None:
+            raise TypeError("fp8 indexer inputs need q_scale and k_scale")
+        _need(q_scale, "q_scale", (torch.float32,), 3)
+        _need(k_scale, "k_scale", (torch.float32,), 2)
+        _shape(q_scale, "q_scale", (B, T, H))
+        _shape(k_scale, "k_scale", (B, Lmax))
+    elif q_scale is not None or k_scale is not None:
+        raise TypeError("bf16 indexer inputs take no scales")
+    _same_device(q, ("w", w), ("k", k), ("ctx_len", ctx_len), ("q_scale", q_scale),
+                 ("k_scale", k_scale))
+    return B, T, H, D, Lmax
+
+
 def ld_for(Lmax: int) -> int:
     return (Lmax + 3) // 4 * 4
 
@@ -77,16 +135,15 @@ def _idx_dtype(q):
 def indexer_scores(q, w, k, ctx_len, q_scale=None, k_scale=None, out=None, stream=None):
     """Lightning-indexer scores [B,T,Lmax] fp32 (a view of a [B,T,ld] buffer)."""
     torch = _torch()
-    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), 4)
-    _need(k, "k", (q.dtype,), 3)
-    _need(w, "w", (torch.float32,), 3)
-    _need(ctx_len, "ctx_len", (torch.int32,), 1)
-    B, T, H, D = q.shape
-    Lmax = k.shape[1]
+    B, T, H, D, Lmax = _indexer_inputs(q, w, k, ctx_len, q_scale, k_scale)
     ld = ld_for(Lmax)
     if out is None:
         out = torch.empty((B, T, ld), dtype=torch.float32, device=q.device)
     _need(out, "out", (torch.float32,), 3)
+    if out.shape[0] != B or out.shape[1] != T or out.shape[2] < Lmax or out.shape[2] % 4:
+        raise TypeError(f"out has shape {tuple(out.shape)}, expected ({B}, {T}, ld) with "
+                        f"ld >= {Lmax} a multiple of 4")
+    _same_device(q, ("out", out))
     lib = library()
     _lib.check(lib.dsa_indexer_scores(_ptr(q), _idx_dtype(q), _ptr(q_scale), _ptr(w), _ptr(k),
                                       _ptr(k_scale), _ptr(ctx_len), B, T, H, D, Lmax,
@@ -106,19 +163,20 @@ def topk(scores, ctx_len, k: int, out=None, workspace=None, stream=None):
         raise TypeError("scores must be a [B,T,L] float32 device tensor")
     if scores.stride(2) != 1 or scores.stride(0) != scores.shape[1] * scores.stride(1):
         raise TypeError("scores rows must be contiguous with a uniform row stride")
-    _need(ctx_len, "ctx_len", (torch.int32,), 1)
     B, T, Lmax = scores.shape
+    _ctx(ctx_len, B)
     ld = scores.stride(1)
     if out is None:
         out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
     _need(out, "out", (torch.int32,), 3)
+    _shape(out, "out", (B, T, k))
+    _same_device(scores, ("ctx_len", ctx_len), ("out", out))
     lib = library()
     need = ctypes.c_size_t(0)
     _lib.check(lib.dsa_topk_workspace_size(B, T, Lmax, k, ctypes.byref(need)))
-    ws = workspace if workspace is not None else torch.zeros(
-        max(need.value, 1), dtype=torch.uint8, device=scores.device)
+    ws = _workspace(workspace, need.value, scores.device, zero=True)
     _lib.check(lib.dsa_topk(_ptr(scores), ld, _ptr(ctx_len), B, T, Lmax, k, _ptr(out),
-                            _ptr(ws), need.value, _stream(stream)))
+                            _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -141,21 +199,17 @@ def indexer_topk(q, w, k_cache, ctx_len, k: int, q_scale=None, k_scale=None, out
     indexer_topk_workspace_size bytes) must start zero-filled; calls leave the
     part that must start at zero as they found it."""
     torch = _torch()
-    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn), 4)
-    _need(k_cache, "k_cache", (q.dtype,), 3)
-    _need(w, "w", (torch.float32,), 3)
-    _need(ctx_len, "ctx_len", (torch.int32,), 1)
-    B, T, H, D = q.shape
-    Lmax = k_cache.shape[1]
+    B, T, H, D, Lmax = _indexer_inputs(q, w, k_cache, ctx_len, q_scale, k_scale)
     if out is None:
         out = torch.empty((B, T, k), dtype=torch.int32, device=q.device)
     _need(out, "out", (torch.int32,), 3)
+    _shape(out, "out", (B, T, k))
+    _same_device(q, ("out", out))
     lib = library()
     dt = _idx_dtype(q)
     need = ctypes.c_size_t(0)
     _lib.check(lib.dsa_indexer_topk_workspace_size(B, T, H, D, dt, Lmax, k, ctypes.byref(need)))
-    ws = workspace if workspace is not None else torch.zeros(need.value, dtype=torch.uint8,
-                                                             device=q.device)
+    ws = _workspace(workspace, need.value, q.device, zero=True)
     _lib.check(lib.dsa_indexer_topk(_ptr(q), dt, _ptr(q_scale), _ptr(w), _ptr(k_cache),
                                     _ptr(k_scale), _ptr(ctx_len), B, T, H, D, Lmax, k, _ptr(out),
                                     _ptr(ws), ws.numel(), _stream(stream)))
@@ -183,23 +237,30 @@ def sparse_attn(q, kv, idx, ctx_len, scale: float, out=None, lse=None, want_lse=
     _need(q, "q", (torch.bfloat16,), 4)
     _need(kv, "kv", (torch.bfloat16,), 3)
     _need(idx, "idx", (torch.int32,), 3)
-    _need(ctx_len, "ctx_len", (torch.int32,), 1)
     B, T, Hq, d_qk = q.shape
     Lmax = kv.shape[1]
     k = idx.shape[2]
     d_v = 512
+    _shape(kv, "kv", (B, Lmax, d_qk))
+    _shape(idx, "idx", (B, T, k))
+    _ctx(ctx_len, B)
     if out is None:
         out = torch.empty((B, T, Hq, d_v), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", (torch.bfloat16,), 4)
+    _shape(out, "out", (B, T, Hq, d_v))
     if lse is None and want_lse:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), 3)
+        _shape(lse, "lse", (B, T, Hq))
+    _same_device(q, ("kv", kv), ("idx", idx), ("ctx_len", ctx_len), ("out", out), ("lse", lse))
     lib = library()
     need = ctypes.c_size_t(0)
     _lib.check(lib.dsa_sparse_attn_workspace_size(B, T, Hq, k, d_v, ctypes.byref(need)))
-    ws = workspace if workspace is not None else torch.empty(
-        max(need.value, 1), dtype=torch.uint8, device=q.device)
+    ws = _workspace(workspace, need.value, q.device, zero=False)
     _lib.check(lib.dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(idx), _ptr(ctx_len), B, T, Hq, Lmax,
                                    k, d_qk, d_v, float(scale), _ptr(out), _ptr(lse), _ptr(ws),
-                                   need.value, _stream(stream)))
+                                   ws.numel(), _stream(stream)))
     return out, lse
 
 
@@ -255,6 +316,37 @@ def _layer_array(layers):
     return arr
 
 
+def _check_layers(layers, indexer_layers, ctx_len, *, B, T, H, D, Lmax, Hq, idx_dtype,
+                  d_qk=576, d_v=512):
+    """Every tensor a layer entry hands to the C ABI has the stack's shape,
+    dtype and device (the ABI sees only pointers): indexer operands on the
+    layers in `indexer_layers`, attention operands on every layer when Hq > 0."""
+    torch = _torch()
+    _ctx(ctx_len, B)
+    kdt = torch.float8_e4m3fn if idx_dtype == "fp8" else torch.bfloat16
+    for l, L in enumerate(layers):
+        if l in indexer_layers:
+            q_idx, k_idx = L.get("q_idx"), L.get("k_idx")
+            _need(q_idx, f"layer {l} q_idx", (kdt,), 4)
+            _shape(q_idx, f"layer {l} q_idx", (B, T, H, D))
+            got = _indexer_inputs(q_idx, L.get("w"), k_idx, ctx_len, L.get("q_idx_scale"),
+                                  L.get("k_idx_scale"))
+            if got[4] != Lmax:
+                raise TypeError(f"layer {l} k_idx holds {got[4]} rows, expected Lmax = {Lmax}")
+        if Hq > 0:
+            q, kv, out, lse = L.get("q"), L.get("kv"), L.get("out"), L.get("lse")
+            for name, t, dt, shp in (("q", q, torch.bfloat16, (B, T, Hq, d_qk)),
+                                     ("kv", kv, torch.bfloat16, (B, Lmax, d_qk)),
+                                     ("out", out, torch.bfloat16, (B, T, Hq, d_v))):
+                _need(t, f"layer {l} {name}", (dt,), len(shp))
+                _shape(t, f"layer {l} {name}", shp)
+                _same_device(ctx_len, (f"layer {l} {name}", t))
+            if lse is not None:
+                _need(lse, f"layer {l} lse", (torch.float32,), 3)
+                _shape(lse, f"layer {l} lse", (B, T, Hq))
+                _same_device(ctx_len, (f"layer {l} lse", lse))
+
+
 _PROXIES = {"output": _lib.DSA_PROXY_OUTPUT, "miss": _lib.DSA_PROXY_MISS}
 
 
@@ -282,12 +374,13 @@ def reuse_costs(layers: Sequence[Dict], ctx_len, *, B, T, H, D, Lmax, k, Hq=0,
     dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
     shape = StackShape(B, T, H, D, Lmax, k, Hq, d_qk, d_v, dt, float(scale))
     dev = ctx_len.device
+    _check_layers(layers, set(range(n)), ctx_len, B=B, T=T, H=H, D=D, Lmax=Lmax,
+                  Hq=Hq if proxy == "output" else 0, idx_dtype=idx_dtype, d_qk=d_qk, d_v=d_v)
     need = ctypes.c_size_t(0)
     lib = library()
     _lib.check(lib.indexcache_reuse_costs_workspace_size(ctypes.byref(shape), n, _PROXIES[proxy],
                                                          ctypes.byref(need)))
-    ws = workspace if workspace is not None else torch.zeros(need.value, dtype=torch.uint8,
-                                                             device=dev)
+    ws = _workspace(workspace, need.value, dev, zero=True)
     ld = ld_for(Lmax)
     score = torch.empty((B, T, ld), dtype=torch.float32, device=dev)
     cost = torch.empty((n, n), dtype=torch.float64, device=dev)
@@ -340,6 +433,8 @@ class Stack:
         self.pattern = pattern.encode()
         self.n_layers = len(layers)
         self._keep = [layers, ctx_len]
+        _check_layers(layers, {l for l, c in enumerate(pattern) if c == "F"}, ctx_len, B=B, T=T,
+                      H=H, D=D, Lmax=Lmax, Hq=Hq, idx_dtype=idx_dtype, d_qk=d_qk, d_v=d_v)
         self.layers = _layer_array(layers)
         dt = _lib.DSA_FP8_E4M3 if idx_dtype == "fp8" else _lib.DSA_BF16
         flags = 0 if fused_topk else _lib.DSA_STACK_UNFUSED_TOPK
