@@ -466,6 +466,18 @@ class Stack:
                     n_topk_calls=self.stats.n_topk_calls, n_attn_calls=self.stats.n_attn_calls)
 
 
+    def run_noalloc(self, stream=None) -> Dict[str, int]:
+        """The same call through indexcache_run_stack_noalloc: the library's
+        static scratch instead of this object's workspace (shapes up to
+        DSA_NOALLOC_SCRATCH_BYTES of workspace)."""
+        _lib.check(library().indexcache_run_stack_noalloc(
+            self.pattern, self.n_layers, self.layers, ctypes.byref(self.shape),
+            _ptr(self.ctx_len), _ptr(self.idx_buf), _ptr(self.score_buf), self.ld,
+            ctypes.byref(self.stats), _stream(stream)))
+        return dict(n_indexer_calls=self.stats.n_indexer_calls,
+                    n_topk_calls=self.stats.n_topk_calls, n_attn_calls=self.stats.n_attn_calls)
+
+
 def run_stack(pattern: str, layers: List[Dict], ctx_len, **shape) -> Dict:
     """One pass of the IndexCache layer loop; returns stats plus idx_buf."""
     st = Stack(pattern, layers, ctx_len, **shape)

@@ -30,6 +30,7 @@ class StackShape(ctypes.Structure):
                 ("idx_dtype", c_int), ("scale", c_f32), ("flags", c_int)]
 
 DSA_STACK_UNFUSED_TOPK = 1
+DSA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class StackStats(ctypes.Structure):
@@ -59,6 +60,9 @@ SIGNATURES = {
     "indexcache_run_stack": (c_int, [ctypes.c_char_p, c_int, ctypes.POINTER(Layer),
                                      ctypes.POINTER(StackShape), c_vp, c_vp, c_vp, c_i64, c_vp,
                                      ctypes.c_size_t, ctypes.POINTER(StackStats), c_vp]),
+    "indexcache_run_stack_noalloc": (c_int, [ctypes.c_char_p, c_int, ctypes.POINTER(Layer),
+                                             ctypes.POINTER(StackShape), c_vp, c_vp, c_vp, c_i64,
+                                             ctypes.POINTER(StackStats), c_vp]),
     "indexcache_reuse_costs_workspace_size": (c_int, [ctypes.POINTER(StackShape), c_int, c_int,
                                                       c_size_p]),
     "indexcache_reuse_costs": (c_int, [c_int, ctypes.POINTER(Layer), ctypes.POINTER(StackShape),

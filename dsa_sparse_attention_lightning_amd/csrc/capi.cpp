@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launchers.hpp"
@@ -272,6 +273,161 @@ dsa_status_t run_indexer(const void* q, dsa_dtype_t dtype, const float* q_scale,
   return hip_status(e, "indexer launch");
 }
 
+// Validation shared by both stack entry points: pattern, flags, every
+// layer's pointers and sizes; *need receives the workspace bytes.  Nothing
+// is launched.
+dsa_status_t check_stack(const char* fn, const char* pattern, int n_layers,
+                         const dsa_layer_t* layers, const dsa_stack_shape_t* shape,
+                         const int32_t* ctx_len, int32_t* idx_buf, float* score_buf,
+                         int64_t ld_scores, size_t* need) {
+  CHECK(pattern != nullptr && layers != nullptr && shape != nullptr, DSA_ERR_INVALID_ARG,
+        "%s: pattern, layers and shape must be non-NULL", fn);
+  {
+    dsa_status_t st = check_pattern(fn, pattern, n_layers);
+    if (st != DSA_OK) return st;
+  }
+  const dsa_stack_shape_t& s = *shape;
+  CHECK(s.Hq >= 0, DSA_ERR_INVALID_ARG, "%s: Hq must be >= 0", fn);
+  CHECK((s.flags & ~DSA_STACK_UNFUSED_TOPK) == 0, DSA_ERR_INVALID_ARG, "%s: unknown flags 0x%x",
+        fn, (unsigned)s.flags);
+  const bool fused = stack_fuses_topk(shape);
+  {
+    dsa_status_t st = indexcache_stack_workspace_size(shape, need);
+    if (st != DSA_OK) return st;
+  }
+  char what[96];
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    snprintf(what, sizeof(what), "%s (layer %d)", fn, l);
+    if (pattern[l] == 'F') {
+      dsa_status_t st = check_indexer(what, L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
+                                      L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
+                                      score_buf, ld_scores, !fused);
+      if (st != DSA_OK) return st;
+      st = check_topk(what, score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k, idx_buf,
+                      !fused);
+      if (st != DSA_OK) return st;
+    }
+    if (s.Hq > 0) {
+      dsa_status_t st = check_attn(what, L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax,
+                                   s.k, s.d_qk, s.d_v, s.scale, L.out, L.lse);
+      if (st != DSA_OK) return st;
+    }
+  }
+  return DSA_OK;
+}
+
+// The layer loop on a validated stack and a workspace of at least the
+// stack's size: F layers write idx_buf, S layers reuse it, every layer
+// attends when Hq > 0.
+dsa_status_t launch_stack(const char* pattern, int n_layers, const dsa_layer_t* layers,
+                          const dsa_stack_shape_t* shape, const int32_t* ctx_len,
+                          int32_t* idx_buf, float* score_buf, int64_t ld_scores,
+                          void* workspace, size_t workspace_bytes, dsa_stack_stats_t* stats,
+                          hipStream_t stream) {
+  const dsa_stack_shape_t& s = *shape;
+  const bool fused = stack_fuses_topk(shape);
+  const size_t tk_bytes = topk_region(shape);
+  void* attn_ws = workspace ? static_cast<unsigned char*>(workspace) + tk_bytes : nullptr;
+  dsa_stack_stats_t st_local = {0, 0, 0};
+  // When the decode indexer runs and the top-k keeps a per-row histogram, the
+  // indexer fills that histogram as it writes the scores and the top-k skips
+  // its own histogram pass.
+  uint32_t* row_hist = uses_prefill_indexer(s.T, s.H, s.D)
+                           ? nullptr
+                           : dsa::topk_row_hist(workspace, s.B, s.T, s.Lmax, s.k);
+  for (int l = 0; l < n_layers; ++l) {
+    const dsa_layer_t& L = layers[l];
+    if (pattern[l] == 'F' && fused) {  // Full layer, scores kept on chip
+      dsa_status_t st = hip_status(
+          launch_fused_topk(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx, L.k_idx_scale,
+                            ctx_len, s.B, s.T, s.H, s.D, s.Lmax, s.k, idx_buf, workspace,
+                            stream),
+          "fused indexer + top-k launch");
+      if (st != DSA_OK) return st;
+      st_local.n_indexer_calls++;
+      st_local.n_topk_calls++;
+    } else if (pattern[l] == 'F') {  // Full layer: fresh index set into the cache
+      dsa_status_t st = run_indexer(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
+                                    L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
+                                    score_buf, ld_scores, row_hist, stream);
+      if (st != DSA_OK) return st;
+      st_local.n_indexer_calls++;
+      st = hip_status(dsa::launch_topk(score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k,
+                                       idx_buf, workspace, tk_bytes, row_hist != nullptr,
+                                       stream),
+                      "topk launch");
+      if (st != DSA_OK) return st;
+      st_local.n_topk_calls++;
+    }
+    // Shared layer: idx_buf already holds the nearest preceding F layer's set.
+    if (s.Hq > 0) {
+      dsa_status_t st = hip_status(
+          dsa::launch_sparse_attn(L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax, s.k,
+                                  s.scale, L.out, L.lse, attn_ws, workspace_bytes - tk_bytes,
+                                  stream),
+          "sparse attention launch");
+      if (st != DSA_OK) return st;
+      st_local.n_attn_calls++;
+    }
+  }
+  if (stats) *stats = st_local;
+  return ok();
+}
+
+// ---- Static scratch of indexcache_run_stack_noalloc (for callers that
+// cannot allocate).  Each GPU the library runs on holds its own copy of this
+// array until the process ends; host code never passes the array's name to a
+// kernel (on the host it is only a stand-in), but the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+constexpr size_t kNoAllocScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status_t scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  CHECK(dev >= 0 && dev < kMaxDevices, DSA_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(DSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+// Bytes at the start of a stack workspace that must be zero when a call
+// starts: the per-row top-k histograms (4096 32-bit bins per query row).
+size_t stack_zero_prefix(const dsa_stack_shape_t* s) {
+  return (size_t)s->B * s->T * 4096 * sizeof(uint32_t);
+}
+
+__global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = z;
+}
+
+// bytes: a multiple of 16 (workspace regions are 256-byte aligned).
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>(1024, (n16 + 255) / 256);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -454,91 +610,46 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
                                   void* workspace, size_t workspace_bytes,
                                   dsa_stack_stats_t* stats, hipStream_t stream) {
   const char* fn = "indexcache_run_stack";
-  CHECK(pattern != nullptr && layers != nullptr && shape != nullptr, DSA_ERR_INVALID_ARG,
-        "%s: pattern, layers and shape must be non-NULL", fn);
-  {
-    dsa_status_t st = check_pattern(fn, pattern, n_layers);
-    if (st != DSA_OK) return st;
-  }
-  const dsa_stack_shape_t& s = *shape;
-  CHECK(s.Hq >= 0, DSA_ERR_INVALID_ARG, "%s: Hq must be >= 0", fn);
-  CHECK((s.flags & ~DSA_STACK_UNFUSED_TOPK) == 0, DSA_ERR_INVALID_ARG, "%s: unknown flags 0x%x",
-        fn, (unsigned)s.flags);
-  const bool fused = stack_fuses_topk(shape);
   size_t need = 0;
-  {
-    dsa_status_t st = indexcache_stack_workspace_size(shape, &need);
-    if (st != DSA_OK) return st;
-  }
+  dsa_status_t st = check_stack(fn, pattern, n_layers, layers, shape, ctx_len, idx_buf,
+                                score_buf, ld_scores, &need);
+  if (st != DSA_OK) return st;
   CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
         "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
-  // Validate every layer before launching anything.
-  char what[96];
-  for (int l = 0; l < n_layers; ++l) {
-    const dsa_layer_t& L = layers[l];
-    snprintf(what, sizeof(what), "%s (layer %d)", fn, l);
-    if (pattern[l] == 'F') {
-      dsa_status_t st = check_indexer(what, L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
-                                      L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
-                                      score_buf, ld_scores, !fused);
-      if (st != DSA_OK) return st;
-      st = check_topk(what, score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k, idx_buf,
-                      !fused);
-      if (st != DSA_OK) return st;
-    }
-    if (s.Hq > 0) {
-      dsa_status_t st = check_attn(what, L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax,
-                                   s.k, s.d_qk, s.d_v, s.scale, L.out, L.lse);
-      if (st != DSA_OK) return st;
-    }
+  if (stack_fuses_topk(shape) || need) CHECK_PTR(workspace);
+  return launch_stack(pattern, n_layers, layers, shape, ctx_len, idx_buf, score_buf, ld_scores,
+                      workspace, workspace_bytes, stats, stream);
+}
+
+dsa_status_t indexcache_run_stack_noalloc(const char* pattern, int n_layers,
+                                          const dsa_layer_t* layers,
+                                          const dsa_stack_shape_t* shape,
+                                          const int32_t* ctx_len, int32_t* idx_buf,
+                                          float* score_buf, int64_t ld_scores,
+                                          dsa_stack_stats_t* stats, hipStream_t stream) {
+  const char* fn = "indexcache_run_stack_noalloc";
+  size_t need = 0;
+  dsa_status_t st = check_stack(fn, pattern, n_layers, layers, shape, ctx_len, idx_buf,
+                                score_buf, ld_scores, &need);
+  if (st != DSA_OK) return st;
+  CHECK(need <= kNoAllocScratchBytes, DSA_ERR_WORKSPACE,
+        "%s: this shape needs %zu bytes of scratch; the library's static scratch holds %zu "
+        "(use indexcache_run_stack with a workspace)",
+        fn, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(fn, &ws);
+  if (st != DSA_OK) return st;
+  // The scratch keeps whatever the previous call on this GPU left in it: the
+  // part that must start at zero (the top-k row histograms, at its start) is
+  // cleared with a fill kernel, never a memset node, so that the call may be
+  // captured into a graph.
+  const size_t zero = std::min(topk_region(shape), stack_zero_prefix(shape));
+  if (zero) {
+    st = hip_status(launch_zero_fill(ws, zero, stream), "scratch clear launch");
+    if (st != DSA_OK) return st;
   }
-  if (fused) CHECK_PTR(workspace);
-  const size_t tk_bytes = topk_region(shape);
-  void* attn_ws = workspace ? static_cast<unsigned char*>(workspace) + tk_bytes : nullptr;
-  dsa_stack_stats_t st_local = {0, 0, 0};
-  // When the decode indexer runs and the top-k keeps a per-row histogram, the
-  // indexer fills that histogram as it writes the scores and the top-k skips
-  // its own histogram pass.
-  uint32_t* row_hist = uses_prefill_indexer(s.T, s.H, s.D)
-                           ? nullptr
-                           : dsa::topk_row_hist(workspace, s.B, s.T, s.Lmax, s.k);
-  for (int l = 0; l < n_layers; ++l) {
-    const dsa_layer_t& L = layers[l];
-    if (pattern[l] == 'F' && fused) {  // Full layer, scores kept on chip
-      dsa_status_t st = hip_status(
-          launch_fused_topk(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx, L.k_idx_scale,
-                            ctx_len, s.B, s.T, s.H, s.D, s.Lmax, s.k, idx_buf, workspace,
-                            stream),
-          "fused indexer + top-k launch");
-      if (st != DSA_OK) return st;
-      st_local.n_indexer_calls++;
-      st_local.n_topk_calls++;
-    } else if (pattern[l] == 'F') {  // Full layer: fresh index set into the cache
-      dsa_status_t st = run_indexer(L.q_idx, s.idx_dtype, L.q_idx_scale, L.w, L.k_idx,
-                                    L.k_idx_scale, ctx_len, s.B, s.T, s.H, s.D, s.Lmax,
-                                    score_buf, ld_scores, row_hist, stream);
-      if (st != DSA_OK) return st;
-      st_local.n_indexer_calls++;
-      st = hip_status(dsa::launch_topk(score_buf, ld_scores, ctx_len, s.B, s.T, s.Lmax, s.k,
-                                       idx_buf, workspace, tk_bytes, row_hist != nullptr,
-                                       stream),
-                      "topk launch");
-      if (st != DSA_OK) return st;
-      st_local.n_topk_calls++;
-    }
-    // Shared layer: idx_buf already holds the nearest preceding F layer's set.
-    if (s.Hq > 0) {
-      dsa_status_t st = hip_status(
-          dsa::launch_sparse_attn(L.q, L.kv, idx_buf, ctx_len, s.B, s.T, s.Hq, s.Lmax, s.k,
-                                  s.scale, L.out, L.lse, attn_ws, workspace_bytes - tk_bytes,
-                                  stream),
-          "sparse attention launch");
-      if (st != DSA_OK) return st;
-      st_local.n_attn_calls++;
-    }
-  }
-  if (stats) *stats = st_local;
-  return ok();
+  return launch_stack(pattern, n_layers, layers, shape, ctx_len, idx_buf, score_buf, ld_scores,
+                      ws, kNoAllocScratchBytes, stats, stream);
 }
 
 dsa_status_t indexcache_reuse_costs_workspace_size(const dsa_stack_shape_t* s, int n_layers,

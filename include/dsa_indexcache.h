@@ -269,6 +269,32 @@ dsa_status_t indexcache_run_stack(const char* pattern, int n_layers, const dsa_l
                                   dsa_stack_stats_t* stats, hipStream_t stream);
 
 /*
+ * indexcache_run_stack without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, validation, kernels and
+ * results as indexcache_run_stack; the workspace is instead a static device
+ * array inside the library of DSA_NOALLOC_SCRATCH_BYTES bytes, which each GPU
+ * the library runs on holds from the module's load until the process ends.
+ * The call allocates and frees nothing.  A shape whose
+ * indexcache_stack_workspace_size exceeds DSA_NOALLOC_SCRATCH_BYTES is
+ * rejected with DSA_ERR_WORKSPACE before anything is launched (the decode
+ * workloads need at most about 33 MiB: batch 64 x 32K context, 128 heads).
+ * The scratch belongs to the device current at the call (the stream's
+ * device); it keeps the previous call's contents, and each call first clears
+ * the part that must start at zero with a small fill kernel on `stream` (no
+ * memset node, so the call can be captured).  Calls that overlap on one GPU
+ * (other threads or streams, no ordering between them) share that scratch
+ * and race; order them on one stream.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status_t indexcache_run_stack_noalloc(const char* pattern, int n_layers,
+                                          const dsa_layer_t* layers,
+                                          const dsa_stack_shape_t* shape,
+                                          const int32_t* ctx_len, int32_t* idx_buf,
+                                          float* score_buf, int64_t ld_scores,
+                                          dsa_stack_stats_t* stats, hipStream_t stream);
+
+/*
  * Training-free pattern search (technical summary §2, part A of the two
  * configuration approaches: start from all-F and convert, one layer at a
  * time, the layer whose switch to S raises the calibration loss least).
