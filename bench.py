@@ -279,6 +279,130 @@ def decode_bench(args, dev):
     return s, layers, res, cut, kernels, roof
 
 
+def oracle_layer_seconds(s, layers, kinds, budget_s, b=0):
+    """Wall time of the fp64 oracle on sequence b of a decode workload: one
+    F layer (indexer + top-k + attention) and one S layer (attention over the
+    F layer's set), each repeated while the budget lasts; returns the mean
+    seconds per F and per S layer and the host threads the oracle used."""
+    import numpy as np
+    import oracle
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+
+    def real(t, sc=None):
+        return (oracle.bf16_bits_to_f64(gen.bits(t)) if sc is None else
+                oracle.dequant_fp8_rows(gen.bits(t), sc.cpu().numpy()))
+
+    L = layers[0]
+    qs = L["q_idx_scale"][b:b + 1] if L["q_idx_scale"] is not None else None
+    ks = L["k_idx_scale"][b:b + 1] if L["k_idx_scale"] is not None else None
+    q_idx = real(L["q_idx"][b:b + 1], qs)
+    k_idx = real(L["k_idx"][b:b + 1], ks)
+    w = L["w"][b:b + 1].cpu().double().numpy()
+    q = real(L["q"][b:b + 1])
+    kv = real(L["kv"][b:b + 1])
+    ctx = [s.ctx]
+    t_f, t_s = [], []
+    start = time.time()
+    idx = None
+    while (not t_f or not t_s) or (time.time() - start < budget_s and len(t_f) < 3):
+        t0 = time.perf_counter()
+        idx = oracle.topk(oracle.indexer_scores(q_idx, w, k_idx, ctx), ctx, s.k)
+        oracle.sparse_attn(q, kv, idx, ctx, s.scale, s.d_v)
+        t_f.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        oracle.sparse_attn(q, kv, idx, ctx, s.scale, s.d_v)
+        t_s.append(time.perf_counter() - t0)
+    return float(np.mean(t_f)), float(np.mean(t_s)), blas_threads()
+
+
+def batched_decode_bench(dev, steps, warmup, cpu_seconds, cfg=1):
+    """The batched decode workload (32 sequences x 32K context, bf16 indexer,
+    8 layers): the configured pattern FSSSFSSS against all-F, per-kernel times
+    with their roofline fractions, and the fp64 oracle's time per token."""
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    s = gen.CONFIGS[cfg]
+    layers = build_decode_workload(s, dev)
+    ctx = gen.ctx_lens(s, dev)
+    out = {"workload": f"{s.name}: {s.n_layers} layers, batch {s.B}, context {s.ctx}, indexer "
+                       f"{s.H}x{s.D} {s.idx_dtype}, top-{s.k}, MLA {s.Hq} heads x {s.d_qk} bf16"}
+    for name, p in (("config", s.pattern), ("all-F", "F" * s.n_layers)):
+        st = dsa.Stack(p, layers, ctx, **shape_kw(s))
+        ms, stats = time_stack(st, steps, warmup)
+        st_i = dsa.Stack(p, layers, ctx, **shape_kw(s, attn=False))
+        ms_i, _ = time_stack(st_i, steps, warmup)
+        out[name] = dict(pattern=p, ms_per_step=round(ms, 4),
+                         tokens_per_s=round(s.B / (ms * 1e-3), 1),
+                         n_indexer_calls=stats["n_indexer_calls"],
+                         indexer_topk_us_per_layer=round(ms_i * 1e3 / s.n_layers, 3),
+                         indexer_topk_us_per_group4=round(ms_i * 1e3 / (s.n_layers / 4), 3))
+        log(f"batched decode {name:6s} {ms:7.3f} ms/step {s.B / (ms * 1e-3):8.0f} tok/s  "
+            f"indexer+topk {ms_i * 1e3 / s.n_layers:6.2f} us/layer")
+        del st, st_i
+    out["fsss_vs_allf_indexer_topk_cut"] = round(
+        1 - out["config"]["indexer_topk_us_per_layer"] / out["all-F"]["indexer_topk_us_per_layer"],
+        4)
+    idx = torch.empty((s.B, s.T, s.k), dtype=torch.int32, device=dev)
+    f_layers = [l for l, c in enumerate(s.pattern) if c == "F"]
+    fz_ws = torch.zeros(dsa.indexer_topk_workspace_size(s.B, s.T, s.H, s.D, s.Lmax, s.k,
+                                                        s.idx_dtype), dtype=torch.uint8,
+                        device=dev)
+    score = torch.empty((s.B, s.T, dsa.ld_for(s.Lmax)), dtype=torch.float32, device=dev)
+
+    def run_fused(i=0):
+        L = layers[i % s.n_layers]
+        dsa.indexer_topk(L["q_idx"], L["w"], L["k_idx"], ctx, s.k, L["q_idx_scale"],
+                         L["k_idx_scale"], out=idx, workspace=fz_ws)
+
+    def run_idx(i=0):
+        L = layers[i % s.n_layers]
+        dsa.indexer_scores(L["q_idx"], L["w"], L["k_idx"], ctx, L["q_idx_scale"],
+                           L["k_idx_scale"], out=score)
+
+    at_ws = torch.zeros(max(1, dsa.sparse_attn_workspace_size(s.B, s.T, s.Hq, s.k)),
+                        dtype=torch.uint8, device=dev)
+
+    def run_attn(i=0):
+        L = layers[i % s.n_layers]
+        dsa.sparse_attn(L["q"], L["kv"], idx, ctx, s.scale, out=L["out"], lse=L["lse"],
+                        workspace=at_ws)
+
+    reps = 3 * s.n_layers
+    t_f = event_time_ms(run_fused, reps)
+    t_i = event_time_ms(run_idx, reps)
+    t_a = event_time_ms(run_attn, reps)
+    ib = indexer_bytes(s)
+    fb = ib - s.B * s.T * s.Lmax * 4 + s.B * s.T * s.k * 4
+    ab, af = attn_bytes_flops(s)
+    out["kernels"] = {
+        "indexer_topk": dict(us=round(t_f * 1e3, 3), bytes=fb,
+                             frac_hbm=round(fb / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             launches_per_step=len(f_layers)),
+        "indexer_decode": dict(us=round(t_i * 1e3, 3), bytes=ib,
+                               frac_hbm=round(ib / (t_i * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               launches_per_step=0),
+        "sparse_mla": dict(us=round(t_a * 1e3, 3), bytes=ab, flops=af,
+                           frac_hbm=round(ab / (t_a * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           frac_bf16_mfma=round(af / (t_a * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           launches_per_step=s.n_layers)}
+    for k_, v in out["kernels"].items():
+        log(f"batched decode kernel {k_:15s} {v['us']:8.2f} us  {v['frac_hbm']:.1%} of HBM peak")
+    del fz_ws, at_ws, score
+    if cpu_seconds > 0:
+        sf, ss, thr = oracle_layer_seconds(s, layers, s.pattern, cpu_seconds)
+        nF = s.pattern.count("F")
+        per_token = nF * sf + (s.n_layers - nF) * ss
+        out["cpu_oracle"] = dict(seconds_per_F_layer=round(sf, 4), seconds_per_S_layer=round(ss, 4),
+                                 tokens_per_s=round(1.0 / per_token, 4), threads=thr,
+                                 sample=f"sequence 0 of {s.B}: one F and one S layer timed, "
+                                        f"projected to {nF} F + {s.n_layers - nF} S layers")
+        log(f"batched decode cpu oracle: {out['cpu_oracle']['tokens_per_s']} tokens/s")
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def reuse_overlap(own, reused) -> float:
     """Share of one row's own selection (the set its layer's indexer and
     top-k pick) that the reused set of the nearest F layer also holds:
@@ -293,7 +417,7 @@ def reuse_overlap(own, reused) -> float:
     return float(np.isin(a, b[b >= 0]).sum()) / a.size
 
 
-def pattern_sweep(dev, steps, warmup, cfg=4):
+def pattern_sweep(dev, steps, warmup, cfg=4, cpu_seconds=0.0):
     """The pattern sweep near maximum context: step time, indexer+top-k time
     per layer, and the overlap between the index set each S layer reuses and
     the set its own indexer would have produced (rows and S layers averaged)."""
@@ -332,13 +456,48 @@ def pattern_sweep(dev, steps, warmup, cfg=4):
                         reuse_overlap=round(float(np.nanmean(ovs)), 4) if ovs else None)
         log(f"sweep {key:9s} {ms:7.3f} ms/step  indexer+topk {ms_i * 1e3 / s.n_layers:7.2f} "
             f"us/layer  overlap {out[key]['reuse_overlap']}")
+    cpu = None
+    if cpu_seconds > 0:
+        sf, ss, thr = oracle_layer_seconds(s, layers, s.pattern, cpu_seconds)
+        cpu = dict(seconds_per_F_layer=round(sf, 4), seconds_per_S_layer=round(ss, 4),
+                   threads=thr, sample=f"sequence 0 of {s.B}: one F and one S layer timed, "
+                                       f"projected to each pattern's F and S layers")
+        for key, v in out.items():
+            nF = v["n_indexer_calls"]
+            cpu[f"tokens_per_s_{key}"] = round(1.0 / (nF * sf + (s.n_layers - nF) * ss), 4)
+        log(f"sweep cpu oracle: {sf:.3f} s per F layer, {ss:.3f} s per S layer")
     del layers
     torch.cuda.empty_cache()
     return dict(workload=f"{s.name}: {s.n_layers} layers, batch {s.B}, context {s.ctx}",
-                patterns=out)
+                patterns=out, cpu_oracle=cpu)
 
 
-def prefill_bench(dev, reps=5):
+def prefill_oracle_sample(s, qi, ki, n_rows=8):
+    """The fp64 oracle's indexer scores and full-sort top-k for n_rows query
+    rows of the prefill chunk (the last rows: the most visible keys), timed
+    and projected to the whole chunk by the rows' visible-key counts."""
+    import numpy as np
+    import oracle
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    rows = list(range(s.T - n_rows, s.T))
+    q = oracle.dequant_fp8_rows(gen.bits(qi.q[:, rows]), qi.q_scale[:, rows].cpu().numpy())
+    w = qi.w[:, rows].cpu().double().numpy()
+    k = oracle.dequant_fp8_rows(gen.bits(ki.k), ki.k_scale.cpu().numpy())
+    pos0 = s.ctx - s.T
+    t0 = time.perf_counter()
+    # a context that ends at the last sampled row: rows sit at pos0 + rows[i]
+    sc = oracle.indexer_scores(q, w, k, [s.ctx])
+    oracle.topk(sc, [s.ctx], s.k)
+    dt = time.perf_counter() - t0
+    seen = sum(pos0 + r + 1 for r in rows)
+    total = sum(pos0 + t + 1 for t in range(s.T))
+    return dict(seconds_sample=round(dt, 3), rows_sampled=n_rows,
+                projected_seconds_per_chunk=round(dt * total / seen, 1), threads=blas_threads(),
+                sample=f"query rows {rows[0]}..{rows[-1]} of the {s.T}-row chunk (fp64 numpy, "
+                       f"indexer + full-sort top-k), projected by visible keys")
+
+
+def prefill_bench(dev, reps=5, cpu=True):
     import torch
     import dsa_sparse_attention_lightning_amd as dsa
     from dsa_sparse_attention_lightning_amd import inputs as gen
@@ -366,14 +525,19 @@ def prefill_bench(dev, reps=5):
         pairs = sum(pos0 + t + 1 for t in range(s.T))
         flops = 2.0 * s.H * s.D * pairs * s.B
         tf = flops / (t_i * 1e-3) / 1e12
+        own_peak = FP8_PEAK_TFLOPS if dt == "fp8" else BF16_PEAK_TFLOPS
         out[dt] = dict(indexer_ms=round(t_i, 4), topk_ms=round(t_k, 4),
                        fused_indexer_topk_ms=round(t_f, 4),
                        algorithmic_tflop=round(flops / 1e12, 4), tflops=round(tf, 1),
+                       frac_own_dtype_peak=round(tf / own_peak, 4),
                        frac_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4),
                        frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
-        log(f"prefill {dt}: indexer {t_i:.3f} ms ({tf:.0f} TFLOP/s, "
-            f"{tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak), top-k {t_k:.3f} ms, fused indexer + "
-            f"top-k {t_f:.3f} ms")
+        target = " (the >= 50% target applies to this bf16 kernel)" if dt == "bf16" else ""
+        log(f"prefill {dt}: indexer {t_i:.3f} ms ({tf:.0f} TFLOP/s = {tf / own_peak:.1%} of the "
+            f"{dt} MFMA peak{target}), top-k {t_k:.3f} ms, fused indexer + top-k {t_f:.3f} ms")
+        if cpu and dt == "fp8":
+            out[dt]["cpu_oracle"] = prefill_oracle_sample(s, qi, ki)
+            log(f"prefill cpu oracle: {out[dt]['cpu_oracle']}")
         del qi, ki, score, idx
         torch.cuda.empty_cache()
     return out
@@ -413,6 +577,97 @@ def prefill_stack_bench(dev, n_layers=4, reps=3):
             f"indexer+top-k {ms_i:.2f} ms, attention {att:.2f} ms/layer")
     out["speedup_fsss_vs_allf"] = round(out["all-F"]["ms_per_chunk"] / out["FSSS"]["ms_per_chunk"], 3)
     del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill_context_bench(dev, ctx_final=196608, chunk=8192):
+    """Whole-context chunked prefill under IndexCache: a prompt of ctx_final
+    tokens taken in chunks of `chunk` tokens through the 48-layer stack of
+    the long-context workload (fp8 indexer 64x128, top-2048, 128-head MLA).
+    Each chunk appends its latent rows and indexer keys to every layer's
+    caches (KV append, T = chunk), then runs the stack over the grown context.
+    The full pass is timed for the 12-F pattern and for all-F, and again
+    without attention (indexer + top-k only), which gives the indexer + top-k
+    share of prefill time.  One pass each (about 40 s of GPU time in all)."""
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    from dsa_sparse_attention_lightning_amd import inputs as gen
+    base = gen.CONFIGS[3]
+    n_chunks = ctx_final // chunk
+    s = gen.Shape(6, "chunked prefill", base.n_layers, base.pattern, B=1, T=chunk,
+                  ctx=ctx_final, H=base.H, D=base.D, idx_dtype=base.idx_dtype, k=base.k,
+                  Hq=base.Hq)
+    t0 = time.time()
+    qi = gen.make_indexer_query(s, dev)
+    kb = gen.randn((s.Lmax, s.D), gen.seed_of(s.cfg_id, 0, "k_base"), dev)
+    layers, src = [], []
+    for l in range(s.n_layers):
+        # fp32 rows a projection would produce: indexer keys correlated across
+        # layers as in the other workloads, latent rows N(0,1)
+        k_src = 0.95 * kb + 0.31 * gen.randn((s.Lmax, s.D), gen.seed_of(s.cfg_id, l, "k_noise"),
+                                            dev)
+        kv_src = gen.randn((s.Lmax, s.d_qk), gen.seed_of(s.cfg_id, l, "kv"), dev)
+        q = gen.randn((1, chunk, s.Hq, s.d_qk), gen.seed_of(s.cfg_id, l, "q"), dev).to(
+            torch.bfloat16)
+        src.append((kv_src[None], k_src[None]))
+        layers.append(dict(q_idx=qi.q, q_idx_scale=qi.q_scale, w=qi.w,
+                           k_idx=torch.zeros((1, s.Lmax, s.D), dtype=torch.float8_e4m3fn,
+                                             device=dev),
+                           k_idx_scale=torch.ones((1, s.Lmax), dtype=torch.float32, device=dev),
+                           q=q, kv=torch.zeros((1, s.Lmax, s.d_qk), dtype=torch.bfloat16,
+                                               device=dev),
+                           out=torch.empty((1, chunk, s.Hq, s.d_v), dtype=torch.bfloat16,
+                                           device=dev)))
+    del kb
+    torch.cuda.synchronize()
+    log(f"chunked prefill workload built in {time.time() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB on device)")
+    # one context-length tensor, set on the stream before each chunk (the
+    # stack's buffers are sized for the whole prompt)
+    ctx_t = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def one_pass(pattern, attn):
+        st = dsa.Stack(pattern, layers, ctx_t, **shape_kw(s, attn))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks + 1)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for c in range(n_chunks):
+            rows = slice(c * chunk, (c + 1) * chunk)
+            ctx_t.fill_((c + 1) * chunk)
+            for l, L in enumerate(layers):
+                dsa.kv_append(ctx_t, src[l][0][:, rows], L["kv"], src[l][1][:, rows],
+                              L["k_idx"], L["k_idx_scale"])
+            st.run()
+            e[c + 1].record()
+        e[-1].synchronize()
+        per = [e[c].elapsed_time(e[c + 1]) for c in range(n_chunks)]
+        del st
+        return sum(per), per
+
+    # warm-up: the first chunk once
+    ctx_t.fill_(chunk)
+    warm = dsa.Stack(s.pattern, layers, ctx_t, **shape_kw(s))
+    warm.run()
+    torch.cuda.synchronize()
+    del warm
+    out = {"workload": f"{s.name}: prompt of {ctx_final} tokens in {n_chunks} chunks of {chunk}, "
+                       f"{s.n_layers} layers, indexer {s.H}x{s.D} {s.idx_dtype}, top-{s.k}, "
+                       f"MLA {s.Hq} heads x {s.d_qk} bf16, KV append per chunk"}
+    for name, p in (("config", s.pattern), ("all-F", "F" * s.n_layers)):
+        ms, per = one_pass(p, True)
+        ms_i, _ = one_pass(p, False)
+        out[name] = dict(pattern=p, prefill_s=round(ms / 1e3, 3),
+                         tokens_per_s=round(ctx_final / (ms * 1e-3), 1),
+                         first_chunk_ms=round(per[0], 2), last_chunk_ms=round(per[-1], 2),
+                         indexer_topk_append_s=round(ms_i / 1e3, 3),
+                         indexer_topk_share=round(ms_i / ms, 4))
+        log(f"chunked prefill {name}: {ms / 1e3:.2f} s for {ctx_final} tokens "
+            f"(chunks {per[0]:.1f} .. {per[-1]:.1f} ms), indexer+top-k(+append) "
+            f"{ms_i / 1e3:.2f} s = {ms_i / ms:.1%}")
+    out["speedup_config_vs_allf"] = round(out["all-F"]["prefill_s"] / out["config"]["prefill_s"],
+                                          3)
+    del layers, src, qi
     torch.cuda.empty_cache()
     return out
 
@@ -524,16 +779,68 @@ def kv_append_bench(dev, reps=200):
     return out
 
 
+def environment():
+    """Where the numbers were taken: GPU, gfx target, ROCm and torch versions,
+    the GPU shader clock as rocm-smi reports it, host CPU model and threads."""
+    import torch
+    env = {}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        env.update(gpu=p.name, gfx_target=getattr(p, "gcnArchName", None),
+                   compute_units=p.multi_processor_count,
+                   hbm_gib=round(p.total_memory / 2**30, 1))
+    except Exception as e:  # pragma: no cover - reported, not fatal
+        env["gpu_error"] = str(e)
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    env["torch"] = torch.__version__
+    # shader / memory clock levels the driver offers (sysfs text); the clock a
+    # kernel actually runs at under load is read from hardware counters
+    # (GRBM_GUI_ACTIVE over the dispatch time) in the profile summaries
+    clocks = {}
+    try:
+        import glob
+        for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+            for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+                path = os.path.join(dev_dir, name)
+                if os.path.exists(path):
+                    lines = [l.strip().rstrip("*").strip() for l in open(path) if l.strip()]
+                    clocks[name[7:] + "_levels"] = [l.split(":", 1)[-1].strip() for l in lines]
+            if clocks:
+                break
+    except OSError as e:  # pragma: no cover
+        clocks = {"error": str(e)}
+    env["gpu_clocks"] = clocks
+    try:
+        models = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                  if l.startswith("model name")]
+        env["host_cpu"] = models[0] if models else None
+    except OSError:
+        env["host_cpu"] = None
+    env["host_cpus"] = os.cpu_count()
+    try:
+        env["host_cpus_usable"] = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        env["host_cpus_usable"] = None
+    return env
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(s, layers, budget_s):
     """The fp64 oracle, as it stands, on sequence 0 of the same workload."""
     import numpy as np
     import oracle
     from dsa_sparse_attention_lightning_amd import inputs as gen
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     b = 0
     t_f, t_s = [], []
     idx = None
@@ -584,6 +891,12 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the 196K-context pattern sweep")
     ap.add_argument("--no-search", action="store_true", help="skip the pattern-search leg")
     ap.add_argument("--no-kv-append", action="store_true", help="skip the KV-append leg")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batched-decode leg (32 x 32K, bf16 indexer)")
+    ap.add_argument("--no-prefill-context", action="store_true",
+                    help="skip the whole-context chunked prefill leg (196608 tokens)")
+    ap.add_argument("--prefill-context-only", action="store_true",
+                    help="run only the whole-context chunked prefill leg")
     ap.add_argument("--search-only", action="store_true",
                     help="run only the pattern-search leg and print its JSON object")
     ap.add_argument("--kv-append-only", action="store_true",
@@ -622,18 +935,31 @@ def main():
     if args.kv_append_only:
         print(json.dumps({"kv_append": kv_append_bench(dev)}), flush=True)
         return
+    if args.prefill_context_only:
+        print(json.dumps({"prefill_context": prefill_context_bench(dev)}), flush=True)
+        return
     if args.prefill_only:
-        print(json.dumps({"prefill": prefill_bench(dev),
+        print(json.dumps({"prefill": prefill_bench(dev, cpu=False),
                           "prefill_stack": prefill_stack_bench(dev)}), flush=True)
         return
+    env = environment()
+    log(f"environment: {json.dumps(env)}")
     s, layers, res, cut, kernels, roof = decode_bench(args, dev)
     main_res = res["config"]
+    batched = None
+    if not args.no_batched:
+        batched = batched_decode_bench(dev, args.steps, args.warmup,
+                                       0.0 if args.no_cpu_baseline else args.cpu_seconds / 3)
     sweep = None
     if not args.no_sweep:
-        sweep = pattern_sweep(dev, max(5, args.steps // 3), 2)
-    prefill = None if args.no_prefill else prefill_bench(dev)
+        sweep = pattern_sweep(dev, max(5, args.steps // 3), 2,
+                              cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 3)
+    prefill = None if args.no_prefill else prefill_bench(dev, cpu=not args.no_cpu_baseline)
     prefill_stack = None if args.no_prefill else prefill_stack_bench(dev)
     kv_app = None if args.no_kv_append else kv_append_bench(dev)
+    prefill_ctx = None
+    if not (args.no_prefill or args.no_prefill_context):
+        prefill_ctx = prefill_context_bench(dev)
     search = None if args.no_search else pattern_search_bench(dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -660,13 +986,16 @@ def main():
                    "pattern": s.pattern, "batch": s.B, "context": s.ctx},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "environment": env,
         "patterns": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                          for kk, vv in v.items()} for k, v in res.items()},
         "fsss_vs_allf_indexer_topk_cut": round(cut, 4),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
+        "batched_decode": batched,
         "prefill": prefill,
         "prefill_stack": prefill_stack,
+        "prefill_context": prefill_ctx,
         "kv_append": kv_app,
         "pattern_search": search,
         "pattern_sweep": sweep,
