@@ -126,7 +126,10 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave-uniform (readfirstlane): the query row and every buffer resource
+  // built from it are then scalar, so the compiler emits plain buffer
+  // instructions instead of a per-instruction loop over lanes' resources
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 5;
   const int col = lane & 31;
   const int b = blockIdx.z;
