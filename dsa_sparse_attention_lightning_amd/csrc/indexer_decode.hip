@@ -125,36 +125,78 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   // workgroup barriers of the histogram)
   const int tend =
       first < wg_end ? min(tiles_per_wave, (wg_end - first + wstride - 1) / wstride) : 0;
-  if (row_hist) {
-    for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
-    __syncthreads();
-  }
   auto tmap = [&](int j) { return __builtin_amdgcn_readfirstlane(first + j * wstride); };
   // fused: the tile after which a wave hands its bins off (none if < 0)
   const int hand_off = (3 * tend) / 4 - 1;
   const int64_t pos = (int64_t)ctx_len[b] - T + t;
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
-  // Query fragments (operand A) and per-row head weights.
+  // Query fragments (operand A) and per-row head weights, through buffer
+  // resources over this row: every load is unconditional (a head past H reads
+  // zeros and adds nothing), so all of a wave's prologue loads are in flight
+  // together.  They are issued before the first key tiles and their products
+  // w * q_scale are formed after those tiles are requested: the memory counter
+  // completes in order, so that wait covers these loads only and the key
+  // stream starts at once.  (Written with a branch per head, the compiler
+  // waited for each weight in turn before the first key load, and the stream
+  // started 5 to 14 us into the launch.)
   i32x4 qv[HB][NV];
   float wv[HB][16];
+  float qsv[FP8 ? HB : 1][16];
+  {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + (int64_t)row * H * ROWB), 0, H * ROWB, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w + (int64_t)row * H), 0, H * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t qsr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(FP8 ? q_scale + (int64_t)row * H : w), 0, FP8 ? H * 4 : 0, kBufferWord3);
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int head = hb * 32 + col;
-    const uint8_t* qp = q + ((int64_t)row * H + head) * ROWB + g * HALF;
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = hb * 32 + col;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) qv[hb][v] = (head < H) ? ld16(qp + 16 * v) : i32x4{0, 0, 0, 0};
+      for (int v = 0; v < NV; ++v)
+        qv[hb][v] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  qr, head * ROWB + g * HALF + 16 * v, 0, 0));
+      // Accumulator rows r = 4j .. 4j+3 are heads hb*32 + 8j + 4g + 0..3: four
+      // consecutive weights per 16-byte load when H is a multiple of 4 (a
+      // 16-byte load straddling the end of the range would read as zero
+      // whole); otherwise one load per weight.
+      if (H % 4 == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      float wt = 0.f;
-      if (h < H) {
-        wt = w[(int64_t)row * H + h];
-        if (FP8) wt *= q_scale[(int64_t)row * H + h];
+        for (int j = 0; j < 4; ++j) {
+          const int h0 = hb * 32 + 8 * j + 4 * g;
+          const f32x4 wq =
+              __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, h0 * 4, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[hb][4 * j + e] = wq[e];
+          if constexpr (FP8) {
+            const f32x4 sq =
+                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qsr, h0 * 4, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qsv[hb][4 * j + e] = sq[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int h = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          wv[hb][r] =
+              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, h * 4, 0, 0));
+          if constexpr (FP8)
+            qsv[hb][r] =
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qsr, h * 4, 0, 0));
+        }
       }
-      wv[hb][r] = wt;
     }
   }
+  auto fold_scales = [&]() {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv[hb][r] *= qsv[hb][r];
+    }
+  };
 
   const uint8_t* kbase = k + (int64_t)b * Lmax * ROWB;
   const float* ksb = FP8 ? k_scale + (int64_t)b * Lmax : nullptr;
@@ -269,8 +311,15 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       }
     }
   };
+  __builtin_amdgcn_sched_barrier(0);  // the prologue loads go first
   if (tile0 < tend) load(tile0, ba, sa);
   if (tile0 + 1 < tend) load(tile0 + 1, bb, sb);
+  __builtin_amdgcn_sched_barrier(0);  // then the first key tiles
+  if (row_hist) {  // cleared while the first tiles stream in
+    for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
+    __syncthreads();
+  }
+  fold_scales();
   for (int tile = tile0; tile < tend; tile += 3) {
     if (tile + 2 < tend) load(tile + 2, bc, sc_);
     compute(tile, ba, sa);
