@@ -66,6 +66,9 @@ constexpr int kHistBins = 1 << kHistBits;
 // policy 2 marks a load nontemporal.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNT = 2;
+// A byte offset past the end of every buffer here (the range check drops such
+// stores and returns zeros for such loads).
+constexpr int kPastEnd = 1 << 30;
 constexpr int kDeviceScope = 16;  // cache policy sc1: coherent at device scope
 constexpr int kParts = 4;  // independent fma chains of the head sum
 constexpr int kFuseKeys = 8192;        // keys whose scores a fused workgroup keeps in LDS
@@ -215,8 +218,16 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       (void*)(FP8 ? ksb : k_scale), 0, FP8 ? Lmax * 4 : 0, kBufferWord3);
   const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)srow, 0, FUSE ? 0 : Lmax * 4, kBufferWord3);
+  // Every path through the tile loop issues the same vector-memory operations:
+  // a sequence number past the wave's share reads tile `tiles`, wholly beyond
+  // the buffers, which returns zeros without touching memory, and the score
+  // stores of the upper half-wave go to an offset past the end of the row.
+  // The compiler's memory waits are merged over all paths that reach a point,
+  // so with a conditional load or store the steady state inherited the waits
+  // of the last iteration (a full drain of the prefetched tiles inside every
+  // tile's arithmetic).
   auto load = [&](int seq, i32x4(&buf)[NL], float(&bs)[CB]) {
-    const int tile = tmap(seq);
+    const int tile = seq < tend ? tmap(seq) : tiles;
 #pragma unroll
     for (int v = 0; v < NL; ++v)
       buf[v] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -289,12 +300,12 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       const int key = tile * TK + c * 32 + col;
       const bool vis = key <= pos && key < Lmax;
       const float o = vis ? (FP8 ? sc * cs[c] : sc) : -INFINITY;
+      if constexpr (!FUSE)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr,
+                                              col * 4 + (g ? kPastEnd : 0),
+                                              (tile * TK + c * 32) * 4, 0);
       if (g == 0) {
-        if constexpr (FUSE)
-          sbuf[(seq * kDecWaves + wave) * TK + c * 32 + col] = o;
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, col * 4,
-                                                (tile * TK + c * 32) * 4, 0);
+        if constexpr (FUSE) sbuf[(seq * kDecWaves + wave) * TK + c * 32 + col] = o;
         if (row_hist && vis) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);
       }
     }
@@ -312,24 +323,27 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
     }
   };
   __builtin_amdgcn_sched_barrier(0);  // the prologue loads go first
-  if (tile0 < tend) load(tile0, ba, sa);
-  if (tile0 + 1 < tend) load(tile0 + 1, bb, sb);
+  load(tile0, ba, sa);
+  load(tile0 + 1, bb, sb);
   __builtin_amdgcn_sched_barrier(0);  // then the first key tiles
   if (row_hist) {  // cleared while the first tiles stream in
     for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
     __syncthreads();
   }
   fold_scales();
-  for (int tile = tile0; tile < tend; tile += 3) {
-    if (tile + 2 < tend) load(tile + 2, bc, sc_);
+  // Whole rounds of three tiles, then the zero to two left over: the loop has
+  // no exit in its body, so no path into its head skips a round's loads.
+  int tile = tile0;
+  for (; tile + 3 <= tend; tile += 3) {
+    load(tile + 2, bc, sc_);
     compute(tile, ba, sa);
-    if (tile + 1 >= tend) break;
-    if (tile + 3 < tend) load(tile + 3, ba, sa);
+    load(tile + 3, ba, sa);
     compute(tile + 1, bb, sb);
-    if (tile + 2 >= tend) break;
-    if (tile + 4 < tend) load(tile + 4, bb, sb);
+    load(tile + 4, bb, sb);
     compute(tile + 2, bc, sc_);
   }
+  if (tile < tend) compute(tile, ba, sa);
+  if (tile + 1 < tend) compute(tile + 1, bb, sb);
   if constexpr (!FUSE) {
     if (row_hist) {  // add this workgroup's counts to the row's histogram
       __syncthreads();
