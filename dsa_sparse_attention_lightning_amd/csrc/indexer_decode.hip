@@ -66,9 +66,12 @@ constexpr int kHistBins = 1 << kHistBits;
 // policy 2 marks a load nontemporal.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNT = 2;
-// A byte offset past the end of every buffer here (the range check drops such
-// stores and returns zeros for such loads).
-constexpr int kPastEnd = 1 << 30;
+// Buffer accesses here put their whole offset in the vector offset, the part
+// the compiler documents as range-checked (gfx950 also checks the scalar
+// offset, but nothing here relies on that): a load past the end returns zeros
+// without touching memory and a store past it is dropped.  kPastEnd (in
+// elements of 4 bytes) lies past the end of every buffer.
+constexpr int kPastEnd = 1 << 28;
 constexpr int kDeviceScope = 16;  // cache policy sc1: coherent at device scope
 constexpr int kParts = 4;  // independent fma chains of the head sum
 constexpr int kFuseKeys = 8192;        // keys whose scores a fused workgroup keeps in LDS
@@ -231,13 +234,13 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
 #pragma unroll
     for (int v = 0; v < NL; ++v)
       buf[v] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             kr, 16 * lane + 1024 * (v & 3),
-                                             tile * kTileBytes + 4096 * (v >> 2), kNT));
+                                             kr, tile * kTileBytes + 1024 * v + 16 * lane, 0,
+                                             kNT));
     if (FP8) {
 #pragma unroll
       for (int c = 0; c < CB; ++c)
         bs[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                              sr, col * 4, (tile * TK + c * 32) * 4, kNT));
+                                              sr, (tile * TK + c * 32 + col) * 4, 0, kNT));
     }
   };
   auto compute = [&](int seq, const i32x4(&raw)[NL], const float(&cs)[CB]) {
@@ -302,8 +305,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       const float o = vis ? (FP8 ? sc * cs[c] : sc) : -INFINITY;
       if constexpr (!FUSE)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr,
-                                              col * 4 + (g ? kPastEnd : 0),
-                                              (tile * TK + c * 32) * 4, 0);
+                                              (key + (g ? kPastEnd : 0)) * 4, 0, 0);
       if (g == 0) {
         if constexpr (FUSE) sbuf[(seq * kDecWaves + wave) * TK + c * 32 + col] = o;
         if (row_hist && vis) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);

@@ -192,10 +192,9 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     }
   }
 
-  // Keys, scales and scores through buffer resources over this sequence: a
-  // per-thread constant offset plus a scalar per-tile offset (no vector
-  // address arithmetic); reads past Lmax return zero, stores past it are
-  // dropped.
+  // Keys, scales and scores through buffer resources over this sequence, the
+  // whole offset in the vector offset (the part the compiler documents as
+  // range-checked): reads past Lmax return zero without touching memory.
   const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(k + (int64_t)b * Lmax * ROWB), 0, Lmax * ROWB, kBufferWord3);
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
@@ -211,11 +210,11 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
 #pragma unroll
     for (int c = 0; c < CH; ++c)
       stage[c] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + c * kPfThreads) * 16,
-                                                       base * ROWB, 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     kr, base * ROWB + (tid + c * kPfThreads) * 16, 0, 0));
     if (FP8 && tid < kPfTile)
       stage_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                              sr, tid * 4, base * 4, 0));
+                                              sr, (base + tid) * 4, 0, 0));
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -306,7 +305,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
         wcount += (uint32_t)__popcll(m);
       } else if (g == 0 && live && key < kc) {
         const float o = key <= pos ? (FP8 ? sc * kss[buf][sb * 32 + col] : sc) : -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, col * 4, kbase * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, key * 4, 0, 0);
       }
     }
     if constexpr (FUSE) {  // tighten the bound every 4 tiles (its own lanes' adds are done)

@@ -56,6 +56,30 @@ def test_indexer_scores(case):
     parity.check_scores(got.cpu().numpy().astype(np.float64), ref, dtype)
 
 
+@pytest.mark.parametrize("T,Lmax,dtype", [(1, 4100, "bf16"), (1, 1000, "fp8"), (5, 1000, "fp8"),
+                                           (3, 4100, "bf16")])
+def test_indexer_scores_tail_tile_stays_in_row(T, Lmax, dtype):
+    """Lmax not a multiple of the key tile and ld = Lmax: the last tile's keys
+    past Lmax must neither reach the next row's scores nor the memory after
+    the last row (a canary after the output)."""
+    B, H, D = 3, 64, 128
+    say("tail tile case", T, Lmax, dtype)
+    qi, ki = make_indexer(B, T, H, D, Lmax, dtype, seed=23 + T + Lmax)
+    ctx = [Lmax, Lmax - 7, max(T, 40)]
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    ld = dsa.ld_for(Lmax)
+    assert ld == Lmax
+    n = B * T * ld
+    buf = torch.full((n + 1024,), 7.0, dtype=torch.float32, device=DEV)
+    out = buf[:n].view(B, T, ld)
+    got = dsa.indexer_scores(qi.q, qi.w, ki.k, ctx_t, qi.q_scale, ki.k_scale, out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[n:] == 7.0).all()), "scores written past the output"
+    ref = oracle.indexer_scores(parity.host_real(qi.q, qi.q_scale), qi.w.cpu().double().numpy(),
+                                parity.host_real(ki.k, ki.k_scale), ctx)
+    parity.check_scores(got.cpu().numpy().astype(np.float64), ref, dtype)
+
+
 def _rand_scores(B, T, L, seed, kind="normal"):
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
