@@ -25,9 +25,11 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 
-# Per-source extra flags (none at present: the attention kernel keeps its
-# O accumulator in AGPRs, pinned there in the source).
-EXTRA = {}
+# Per-source extra flags.  The attention kernel has its first 14 argument
+# dwords preloaded into scalar registers at launch (gfx950 kernel-argument
+# preloading; the code object keeps a fallback that loads them itself), so
+# its first gathers wait on no argument load.
+EXTRA = {"sparse_mla.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"]}
 
 
 def hipcc() -> str:

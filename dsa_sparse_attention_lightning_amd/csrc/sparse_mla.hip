@@ -169,13 +169,15 @@ __device__ __forceinline__ void combine_unit(const __bf16* __restrict__ part_o,
     lse[(int64_t)row * Hq + head] = den > 0.f ? m + logf(den) : -INFINITY;
 }
 
+// The arguments that the first gathers depend on come first: the first 14
+// argument dwords are preloaded into scalar registers at launch (built with
+// -amdgpu-kernarg-preload-count=14), so the gathers wait on no argument load.
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kv, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ ctx_len, int T, int Hq, int Lmax, int k, int rows_per_split,
-    float scale_log2, __bf16* __restrict__ out, float* __restrict__ lse,
-    __bf16* __restrict__ part_o, float* __restrict__ part_lse, int n_split, int head_groups,
-    int n_work, int per_xcd) {
+    const int32_t* __restrict__ idx, const __bf16* __restrict__ kv, const __bf16* __restrict__ q,
+    int T, int k, int rows_per_split, int n_split, int head_groups, int per_xcd, int Lmax, int Hq,
+    const int32_t* __restrict__ ctx_len, float scale_log2, __bf16* __restrict__ out,
+    float* __restrict__ lse, __bf16* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int NT = NW * kWave;
   constexpr int kMaxSplitRows = max_split_rows(NW);
   constexpr int KJ = (kTileLoads + NW - 1) / NW;  // DMA instructions per wave per tile
@@ -192,13 +194,15 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  // Work item w = ((row * n_split) + split) * head_groups + head group.  The
-  // dispatcher deals consecutive workgroups to the 8 XCDs in turn, so
-  // workgroup i runs on XCD i % 8; giving each XCD one contiguous range of
-  // work items keeps a query row's fragments and the rows its head groups
-  // gather together in one XCD's L2 instead of fetching them 8 times.
-  const int bid = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (bid >= n_work) return;
+  // Work item w = ((row * n_split) + split) * head_groups + head group; the
+  // grid holds exactly the work items.  The dispatcher deals consecutive
+  // workgroups to the 8 XCDs in turn, so workgroup i runs on XCD i % 8; when
+  // the work items split into 8 equal ranges (per_xcd > 0) each XCD takes one
+  // contiguous range, which keeps a query row's fragments and the rows its
+  // head groups gather together in one XCD's L2 instead of fetching them 8
+  // times.
+  const int bid = per_xcd > 0 ? (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3)
+                              : (int)blockIdx.x;
   const int hgi = bid % head_groups;
   const int rs = bid / head_groups;
   const int split = rs % n_split;
@@ -221,25 +225,26 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
 
   // ---- Global loads in the order they are needed: the memory counter
   // completes in order, so waiting for the indices must not wait for the
-  // query fragments behind them.  First the context length and the selected
-  // rows of this wave's DMA slots in tiles 0 and 1 and of this thread's share
-  // of the slice (its LDS copy), then the query fragments.
-  const int ctx = ctx_len[b];
-  const int32_t* ib = idx + (int64_t)row * k + j0;
-  int r0[KJ], r1[KJ];
-#pragma unroll
-  for (int j = 0; j < KJ; ++j) {
-    const int rr = gslot[j] >> 16;
-    r0[j] = (rr < nrows) ? ib[rr] : -1;
-    r1[j] = (kRows + rr < nrows) ? ib[kRows + rr] : -1;
-  }
+  // query fragments behind them.  First the selected rows of tiles 0 and 1
+  // (lane l loads row l of the slice; the DMA slots take theirs from it by
+  // cross-lane reads) and this thread's share of the slice (its LDS copy),
+  // then the query fragments.  The slice is read through a buffer resource:
+  // every load is unconditional (past the slice it reads zero, which the
+  // select turns into -1).  Few load instructions matter here: at the start
+  // of the kernel every wave of the CU issues its loads at once, and the
+  // address unit takes them one after another.
+  static_assert(2 * kRows == kWave, "one lane per row of tiles 0 and 1");
+  const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(idx + (int64_t)row * k + j0), 0, nrows * 4, kBufferWord3);
+  auto sel = [&](int j) {
+    const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, j * 4, 0, 0);
+    return j < nrows ? v : -1;
+  };
+  const int first_rows = sel(lane);
   constexpr int kCopy = kMaxSplitRows / NT;
   int rc[kCopy];
 #pragma unroll
-  for (int u = 0; u < kCopy; ++u) {
-    const int j = tid + NT * u;
-    rc[u] = (j < nrows) ? ib[j] : -1;
-  }
+  for (int u = 0; u < kCopy; ++u) rc[u] = sel(tid + NT * u);
   // Query fragments (nothing depends on them until the first tile): operand
   // B of S^T (column = head, reduction = dims); lane group g covers dims
   // [144 g, 144 g + 144), 8 per step.
@@ -249,32 +254,44 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
 #pragma unroll
     for (int i = 0; i < 18; ++i) qf[i] = as_bf16x8(ld16(qp + 8 * i));
   }
+  // Every load above is issued before anything uses an index (left alone,
+  // the compiler starts the first gather's address arithmetic in between, and
+  // the rest of the loads then wait for the first index to arrive).
+  __builtin_amdgcn_sched_barrier(0);
+  int r0[KJ], r1[KJ];
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int rr = gslot[j] >> 16;
+    r0[j] = __builtin_amdgcn_ds_bpermute(4 * rr, first_rows);
+    r1[j] = __builtin_amdgcn_ds_bpermute(4 * (kRows + rr), first_rows);
+  }
 
-  // A selected row is used only if it is a real position visible to the
-  // query (invalid / padding -> -1, whose score bias is -inf).
-  const int64_t pos = (int64_t)ctx - T + t;
-  auto valid = [&](int v) { return (v < 0 || (int64_t)v > pos || v >= Lmax) ? -1 : v; };
   // The DMA goes through a buffer resource over this sequence's latent rows
   // (MUBUF, not FLAT: a FLAT load that writes LDS makes every later LDS wait
-  // of the wave a full drain, which would also wait for this DMA).  Offsets
-  // past the buffer read as zero.
+  // of the wave a full drain, which would also wait for this DMA).  The whole
+  // offset is in the range-checked vector offset, so row -1 (padding, or past
+  // the slice) lies past the buffer: its DMA writes zeros and reads nothing.
   const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(kv + (int64_t)b * Lmax * kDqk), 0, Lmax * kRowBytes, kBufferWord3);
   auto issue_one = [&](unsigned char* tile, int j, int src) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         kvr, (lds_void*)(tile + dma_inst(j) * kWave * 16), 16,
-        (unsigned)(max(src, 0) * kRowBytes + (gslot[j] & 0xffff)), 0, 0, 0);
+        (unsigned)src * kRowBytes + (unsigned)(gslot[j] & 0xffff), 0, 0, 0);
   };
-  // Tiles 0 and 1 are requested together: a slice of 64 rows (the common
-  // decode case) then waits on a single round trip to HBM.
-  if (ntiles > 0) {
+  // Tiles 0 and 1 are requested together as soon as the indices arrive (a
+  // slice of 64 rows, the common decode case, then waits on a single round
+  // trip to HBM).  They do not wait for the context length: a row the query
+  // may not see is gathered all the same and masked by its score bias.  (The
+  // requests are unconditional: a tile past the slice has only rows -1.)
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) issue_one(tileA, j, valid(r0[j]));
-  }
-  if (ntiles > 1) {
+  for (int j = 0; j < KJ; ++j) issue_one(tileA, j, r0[j]);
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) issue_one(tileB, j, valid(r1[j]));
-  }
+  for (int j = 0; j < KJ; ++j) issue_one(tileB, j, r1[j]);
+  // A selected row is used only if it is a real position visible to the
+  // query (invalid / padding -> -1, whose score bias is -inf).
+  const int ctx = ctx_len[b];
+  const int64_t pos = (int64_t)ctx - T + t;
+  auto valid = [&](int v) { return (v < 0 || (int64_t)v > pos || v >= Lmax) ? -1 : v; };
   // LDS copy of the slice's rows (for later tiles' DMA) and score bias.
 #pragma unroll
   for (int u = 0; u < kCopy; ++u) {
@@ -317,10 +334,15 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
     kb = *(const lds_i32x4*)(ap + 16 * kPitch);
   };
   // Rows of a later tile's DMA slots and the score bias of the next tile are
-  // read from LDS one step ahead (clamped: past the slice they are unused).
+  // read from LDS one step ahead (past the slice a row is -1: its DMA reads
+  // nothing).
   auto lookup_rows = [&](int tbase, int (&src)[KJ]) {
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) src[j] = rows[min(tbase + (gslot[j] >> 16), kMaxSplitRows - 1)];
+    for (int j = 0; j < KJ; ++j) {
+      const int r = tbase + (gslot[j] >> 16);
+      const int v = rows[min(r, kMaxSplitRows - 1)];
+      src[j] = r < nrows ? v : -1;
+    }
   };
   auto lookup_bias = [&](int tbase, f32x4& b0, f32x4& b1) {
     const int t0 = min(tbase, kMaxSplitRows - kRows);
@@ -416,6 +438,35 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
   // softmax head of tile n+1 (and its rare O rescale) closes the step.  On
   // the last steps the DMA and S^T touch stale rows and buffers (the buffer
   // resource bounds every offset) and their results are never used.
+  // O^T += V^T . P^T for one tile (P: its buffer; sv: its exponentials),
+  // with the transposing reads 6 fragments ahead.
+  auto pv = [&](const unsigned char* P) {
+    constexpr int kAhead = 6;
+    i32x4 pb;
+    pb[0] = (int)cvt_pk_bf16(sv[0], sv[1]);
+    pb[1] = (int)cvt_pk_bf16(sv[2], sv[3]);
+    pb[2] = (int)cvt_pk_bf16(sv[4], sv[5]);
+    pb[3] = (int)cvt_pk_bf16(sv[6], sv[7]);
+    const bf16x8 pbf = as_bf16x8(pb);
+    v4i16 va[32], vb[32];
+    const unsigned char* vp = P + tr_base;
+#pragma unroll
+    for (int mb = 0; mb < kAhead; ++mb) {
+      va[mb] = tr_read(vp + 32 * mb);
+      vb[mb] = tr_read(vp + 32 * mb + 16 * kPitch);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) {
+      const v4i16 pair[2] = {va[mb], vb[mb]};
+      o[mb] = mfma16_bf16(__builtin_bit_cast(bf16x8, pair), pbf, o[mb]);
+      if (mb + kAhead < 32) {
+        va[mb + kAhead] = tr_read(vp + 32 * (mb + kAhead));
+        vb[mb + kAhead] = tr_read(vp + 32 * (mb + kAhead) + 16 * kPitch);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto step = [&](int n, const unsigned char* P, const unsigned char* Q, unsigned char* D) {
     constexpr int kAhead = 6;
     wait_vm_all();
@@ -452,40 +503,36 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
 #pragma unroll
     for (int j = 18; j < KJ; ++j) issue_one(D, j, src[j]);  // (narrow workgroups)
     l_run += ls;
-    i32x4 pb;
-    pb[0] = (int)cvt_pk_bf16(sv[0], sv[1]);
-    pb[1] = (int)cvt_pk_bf16(sv[2], sv[3]);
-    pb[2] = (int)cvt_pk_bf16(sv[4], sv[5]);
-    pb[3] = (int)cvt_pk_bf16(sv[6], sv[7]);
-    const bf16x8 pbf = as_bf16x8(pb);
-    v4i16 va[32], vb[32];
-    const unsigned char* vp = P + tr_base;
-#pragma unroll
-    for (int mb = 0; mb < kAhead; ++mb) {
-      va[mb] = tr_read(vp + 32 * mb);
-      vb[mb] = tr_read(vp + 32 * mb + 16 * kPitch);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      const v4i16 pair[2] = {va[mb], vb[mb]};
-      o[mb] = mfma16_bf16(__builtin_bit_cast(bf16x8, pair), pbf, o[mb]);
-      if (mb + kAhead < 32) {
-        va[mb + kAhead] = tr_read(vp + 32 * (mb + kAhead));
-        vb[mb + kAhead] = tr_read(vp + 32 * (mb + kAhead) + 16 * kPitch);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    pv(P);
     softmax_head(a0 + a1, b0 + b1, bias0, bias1, n + 1 < ntiles, false);
   };
 
-  // Unrolled by three so that every buffer role is static.
-  for (int n = 0; n < ntiles; n += 3) {
+  // The last tile: its exponentials and O^T += V^T . P^T only (there is no
+  // next tile to score and nothing more to gather).
+  auto last_step = [&](const unsigned char* P) {
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sv[i] = __builtin_amdgcn_exp2f(sv[i] - mref);
+      ls += sv[i];
+    }
+    l_run += ls;
+    pv(P);
+  };
+
+  // Every tile but the last takes a full step, unrolled by three so that
+  // every buffer role is static; tile n sits in buffer n % 3.
+  const int nfull = ntiles - 1;
+  for (int n = 0; n < nfull; n += 3) {
     step(n, tileA, tileB, tileC);
-    if (n + 1 >= ntiles) break;
+    if (n + 1 >= nfull) break;
     step(n + 1, tileB, tileC, tileA);
-    if (n + 2 >= ntiles) break;
+    if (n + 2 >= nfull) break;
     step(n + 2, tileC, tileA, tileB);
+  }
+  if (ntiles > 0) {
+    const int r = nfull % 3;
+    last_step(r == 0 ? tileA : r == 1 ? tileB : tileC);
   }
   wait_vm_all();  // the last steps' DMA may still be writing a tile buffer
   __syncthreads();  // every wave is done with the tiles: they stage the output
@@ -589,11 +636,10 @@ hipError_t launch_attn(const SplitPlan& p, const __bf16* q, const __bf16* kv, co
                        __bf16* out, float* lse, __bf16* part_o, float* part_lse,
                        hipStream_t stream) {
   const int n_work = B * T * p.head_groups * p.n_split;
-  const int per_xcd = (n_work + 7) / 8;
-  const dim3 grid(8 * per_xcd);
-  hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * kWave), 0, stream, q, kv, idx,
-                     ctx_len, T, Hq, Lmax, k, p.rows_per_split, sl2, out, lse, part_o, part_lse,
-                     p.n_split, p.head_groups, n_work, per_xcd);
+  const int per_xcd = n_work % 8 == 0 ? n_work / 8 : 0;
+  hipLaunchKernelGGL((sparse_mla_kernel<NW>), dim3(n_work), dim3(NW * kWave), 0, stream, idx, kv,
+                     q, T, k, p.rows_per_split, p.n_split, p.head_groups, per_xcd, Lmax, Hq,
+                     ctx_len, sl2, out, lse, part_o, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split <= 1) return e;
   hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(B * T, (Hq + kCombHeads - 1) / kCombHeads),
