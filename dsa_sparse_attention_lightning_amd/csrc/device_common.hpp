@@ -138,4 +138,38 @@ __device__ void select_bin(const uint32_t* hist, uint32_t kk, uint32_t* scan, ui
   __syncthreads();
 }
 
+// The same selection by one wave and no barrier (the caller synchronises):
+// lane l sums bins [NB - PER (l + 1), NB - PER l) (PER = NB / 64, read
+// with a per-lane rotation so the lanes spread over the LDS banks), a wave
+// prefix sum finds the lane whose range holds the kk-th largest, and the
+// wave then scans that lane's PER bins one per lane.  Writes {bin, count
+// strictly above it} to sel[0..1]; kk must be in [1, total].
+template <int NB>
+__device__ void wave_select_bin(const uint32_t* hist, uint32_t kk, uint32_t* sel) {
+  constexpr int PER = NB / kWave;
+  constexpr int V = PER / 4;
+  static_assert(PER % 4 == 0 && PER <= kWave && (V & (V - 1)) == 0, "whole vectors per lane");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lo = NB - PER * (lane + 1);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int v = (i + lane) & (V - 1);
+    const uint4 x = *reinterpret_cast<const uint4*>(hist + lo + 4 * v);
+    sum += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint64_t m = __ballot(incl - sum < kk && kk <= incl);
+  const int L = m ? (int)__builtin_ctzll(m) : kWave - 1;
+  const uint32_t base = __builtin_amdgcn_readlane(incl - sum, L);
+  const uint32_t c = lane < PER ? hist[NB - 1 - (L * PER + lane)] : 0u;
+  const uint32_t ci = wave_incl_scan(c) + base;
+  const uint64_t m2 = __ballot(lane < PER && ci - c < kk && kk <= ci);
+  const int j = m2 ? (int)__builtin_ctzll(m2) : 0;
+  if (lane == j) {
+    sel[0] = (uint32_t)(NB - 1 - (L * PER + j));
+    sel[1] = ci - c;
+  }
+}
+
 }  // namespace dsa

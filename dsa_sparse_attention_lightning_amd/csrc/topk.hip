@@ -44,6 +44,7 @@ constexpr int kChWaves = kChThreads / kWave;
 constexpr int kMaxChunks = kTopkMaxChunks;
 constexpr int kPer = 16;         // scores per thread per chunk batch (4096 per workgroup)
 constexpr int kGather = 8;       // candidate loads in flight per thread
+constexpr int kFinGather = 16;   // ... in the decode finish (first batch of every slice)
 
 struct TopkSmem {
   uint32_t hist[kBins1];
@@ -111,21 +112,22 @@ __device__ __forceinline__ void hist_to_lds(const uint32_t* __restrict__ g, uint
 }
 
 // Ordered emission of the selected elements: key > tau, or key == tau and
-// among the first take_eq such elements.  Elements arrive 4 per thread in
-// position order through `fetch(base, key, pos, ok)`.
-template <typename Fetch>
+// among the first take_eq such elements.  Elements arrive E per thread in
+// position order through `fetch(base, key, pos, ok)` (E * kTkThreads < 2^16).
+template <int E = 4, typename Fetch>
 __device__ void emit_selected(int count, uint32_t tau, uint32_t take_eq, int32_t* out,
                               TopkSmem& sm, Fetch fetch) {
+  static_assert(E * kTkThreads < 65536, "per-pass counts fit 16 bits");
   const int tid = threadIdx.x;
   uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < count; base += 4 * kTkThreads) {
-    uint32_t key[4] = {0, 0, 0, 0};
-    int32_t pos[4] = {0, 0, 0, 0};
-    bool ok[4];
-    fetch(base + 4 * tid, key, pos, ok);
+  for (int base = 0; base < count; base += E * kTkThreads) {
+    uint32_t key[E] = {};
+    int32_t pos[E] = {};
+    bool ok[E];
+    fetch(base + E * tid, key, pos, ok);
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < E; ++j) {
       ngt += (ok[j] && key[j] > tau);
       neq += (ok[j] && key[j] == tau);
     }
@@ -133,7 +135,7 @@ __device__ void emit_selected(int count, uint32_t tau, uint32_t take_eq, int32_t
     const uint32_t ex = block_excl_scan<kTkWaves>((ngt << 16) | neq, sm.scan, tot);
     uint32_t gt_b = run_gt + (ex >> 16), eq_b = run_eq + (ex & 0xFFFFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < E; ++j) {
       if (!ok[j]) continue;
       if (key[j] > tau) {
         out[gt_b + min(eq_b, take_eq)] = pos[j];
@@ -148,50 +150,61 @@ __device__ void emit_selected(int count, uint32_t tau, uint32_t take_eq, int32_t
   }
 }
 
-// Steps 3-4 from the LDS list of the M elements in bins >= b1.
-__device__ void finish_from_list(int M, uint32_t b1, uint32_t above1, int k, int32_t* out,
-                                 TopkSmem& sm) {
+// Steps 3-4 from the LDS list of the M elements in bins >= b1.  The second-
+// and third-digit histograms are sm.hist[0, 1024) and [1024, 2048) (zero on
+// entry when `zeroed`); each digit is selected by one wave, so a digit costs
+// two barriers.  The emission takes 8 list entries per thread, so a list of
+// up to 8192 entries is emitted in one ordered pass.
+__device__ __forceinline__ void finish_from_list(int M, uint32_t b1, uint32_t above1, int k, int32_t* out,
+                                 TopkSmem& sm, bool zeroed = false) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
-  __syncthreads();
+  uint32_t* h2 = sm.hist;
+  uint32_t* h3 = sm.hist + kBins2;
+  if (!zeroed) {
+    for (int i = tid; i < 2 * kBins2; i += kTkThreads) sm.hist[i] = 0;
+    __syncthreads();
+  }
   for (int e = tid; e < M; e += kTkThreads) {
     const uint32_t key = sm.list_key[e];
-    if ((key >> 20) == b1) atomicAdd(&sm.hist[(key >> 10) & 1023u], 1u);
+    if ((key >> 20) == b1) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
   }
   __syncthreads();
-  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1, sm.scan, sm.sel);
+  if (tid < kWave) wave_select_bin<kBins2>(h2, (uint32_t)k - above1, sm.sel);
+  __syncthreads();
   const uint32_t b2 = sm.sel[0];
   const uint32_t above2 = sm.sel[1];
-  __syncthreads();
   const uint32_t pre2 = (b1 << 10) | b2;
-  for (int i = tid; i < kBins2; i += kTkThreads) sm.hist[i] = 0;
-  __syncthreads();
   for (int e = tid; e < M; e += kTkThreads) {
     const uint32_t key = sm.list_key[e];
-    if ((key >> 10) == pre2) atomicAdd(&sm.hist[key & 1023u], 1u);
+    if ((key >> 10) == pre2) atomicAdd(&h3[key & 1023u], 1u);
   }
   __syncthreads();
-  select_bin<kBins2, kTkThreads>(sm.hist, (uint32_t)k - above1 - above2, sm.scan, sm.sel);
-  const uint32_t b3 = sm.sel[0];
-  const uint32_t above3 = sm.sel[1];
+  if (tid < kWave) wave_select_bin<kBins2>(h3, (uint32_t)k - above1 - above2, sm.sel + 2);
   __syncthreads();
+  const uint32_t b3 = sm.sel[2];
+  const uint32_t above3 = sm.sel[3];
   const uint32_t tau = (b1 << 20) | (b2 << 10) | b3;
   const uint32_t take_eq = (uint32_t)k - above1 - above2 - above3;
-  emit_selected(M, tau, take_eq, out, sm,
-                [&](int e, uint32_t(&key)[4], int32_t(&p)[4], bool(&ok)[4]) {
+  // (the reads are unconditional, two 16-byte reads per array: entries past
+  // M are stale and masked, and the list has room for 8 kTkThreads entries)
+  static_assert(8 * kTkThreads <= kTkCap, "whole emission pass inside the list");
+  emit_selected<8>(M, tau, take_eq, out, sm,
+                   [&](int e, uint32_t(&key)[8], int32_t(&p)[8], bool(&ok)[8]) {
+                     const uint4 k0 = *reinterpret_cast<const uint4*>(&sm.list_key[e]);
+                     const uint4 k1 = *reinterpret_cast<const uint4*>(&sm.list_key[e + 4]);
+                     const int4 p0 = *reinterpret_cast<const int4*>(&sm.list_pos[e]);
+                     const int4 p1 = *reinterpret_cast<const int4*>(&sm.list_pos[e + 4]);
+                     key[0] = k0.x; key[1] = k0.y; key[2] = k0.z; key[3] = k0.w;
+                     key[4] = k1.x; key[5] = k1.y; key[6] = k1.z; key[7] = k1.w;
+                     p[0] = p0.x; p[1] = p0.y; p[2] = p0.z; p[3] = p0.w;
+                     p[4] = p1.x; p[5] = p1.y; p[6] = p1.z; p[7] = p1.w;
 #pragma unroll
-                  for (int j = 0; j < 4; ++j) {
-                    ok[j] = (e + j) < M;
-                    if (ok[j]) {
-                      key[j] = sm.list_key[e + j];
-                      p[j] = sm.list_pos[e + j];
-                    }
-                  }
-                });
+                     for (int j = 0; j < 8; ++j) ok[j] = (e + j) < M;
+                   });
 }
 
 // Steps 3-4 re-reading the row from memory (list would not fit in LDS).
-__device__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t above1, int k,
+__device__ __forceinline__ void finish_from_row(const float* src, int n, uint32_t b1, uint32_t above1, int k,
                                 int32_t* out, TopkSmem& sm) {
   const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t r = row_rsrc(src, n);
@@ -311,7 +324,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
   __syncthreads();
   for_each_key(r, n, [&](uint32_t key) { atomicAdd(&sm.hist[key >> 20], 1u); });
   __syncthreads();
-  select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
+  if (tid < kWave) wave_select_bin<kBins1>(sm.hist, (uint32_t)k, sm.sel);
+  __syncthreads();
   const uint32_t b1 = sm.sel[0];
   const uint32_t above1 = sm.sel[1];
   const uint32_t listed = above1 + sm.hist[b1];
@@ -468,42 +482,40 @@ __global__ __launch_bounds__(kChThreads) void topk_chunk_collect_kernel(
 // the fused indexer) the threshold bin comes from the finished histogram and
 // the slices may also hold keys below it, which are never emitted; otherwise
 // row_sel holds it (written by the collect pass).
+// (The arguments its first loads need come first: the leading argument
+// dwords are preloaded into scalar registers at launch.)
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
-    int Lmax, int k, int chunk, int n_chunks, uint32_t* __restrict__ hist_g,
-    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
-    const uint32_t* __restrict__ cand_cnt, const uint32_t* __restrict__ row_sel,
-    bool sel_from_hist, int32_t* __restrict__ idx) {
+    uint32_t* __restrict__ hist_g, const uint32_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_pos, const uint32_t* __restrict__ cand_cnt,
+    const int32_t* __restrict__ ctx_len, int T, int Lmax, int chunk, int n_chunks, int k,
+    const uint32_t* __restrict__ row_sel, int sel_from_hist, const float* __restrict__ scores,
+    int64_t ld, int32_t* __restrict__ idx) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   TopkSmem& sm = *reinterpret_cast<TopkSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
-  const int n = visible(ctx_len, row, T, Lmax);
-  int32_t* out = idx + (int64_t)row * k;
   uint32_t* hg = hist_g + (int64_t)row * kBins1;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
-    // the chunk kernels touched nothing for this row, but a fused
-    // histogram from the indexer may have
-    for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
-    return;
-  }
-  // the slice counts, and the row's selection (written by the collect pass)
-  const uint32_t cnt = (tid < n_chunks) ? cand_cnt[(int64_t)row * n_chunks + tid] : 0u;
-  uint32_t b1 = 0, above1 = 0, listed = 0;
-  i32x4 hv = {0, 0, 0, 0};
+  // The slice counts, the histogram and the row's selection (written by
+  // the collect pass when the histogram is not finished): unconditional
+  // loads, through buffer resources where a count or a pointer may be short
+  // (the selection's range is empty when it is not used).
+  const uint32_t cnt = __builtin_amdgcn_raw_buffer_load_b32(
+      __builtin_amdgcn_make_buffer_rsrc((void*)(cand_cnt + (int64_t)row * n_chunks), 0,
+                                        n_chunks * 4, kBufferWord3),
+      tid * 4, 0, 0);
   static_assert(kBins1 == 4 * kTkThreads, "one 16-byte histogram load per thread");
-  if (sel_from_hist)
-    hv = ld16(hg + 4 * tid);
-  else {
-    b1 = row_sel[3 * row];
-    above1 = row_sel[3 * row + 1];
-    listed = row_sel[3 * row + 2];
-  }
+  const i32x4 hv = ld16(hg + 4 * tid);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(row_sel + 3 * (int64_t)row), 0, sel_from_hist ? 0 : 12, kBufferWord3);
+  uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b32(sr, 0, 0, 0);
+  uint32_t above1 = __builtin_amdgcn_raw_buffer_load_b32(sr, 4, 0, 0);
+  uint32_t listed = __builtin_amdgcn_raw_buffer_load_b32(sr, 8, 0, 0);
   // Each slice is copied by its own group of tpc threads.  The first batch
   // of every slice is requested now, before its length is known (slice c
   // starts at c * chunk; entries past its length are ignored), so the copy
-  // does not wait for a second round trip.
+  // does not wait for a second round trip.  These loads and the context
+  // length are all in flight together: the kernel starts on one round trip
+  // to memory.
   const int tpc = kTkThreads / n_chunks;
   const int cq = tid / tpc;  // this thread's slice (none when >= n_chunks)
   const int sub = tid - cq * tpc;
@@ -511,20 +523,32 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   const int cap = (int)min((int64_t)chunk, (int64_t)Lmax - base);  // room of the slice
   const uint32_t* ck = cand_key + (int64_t)row * Lmax + base;
   const int32_t* cp = cand_pos + (int64_t)row * Lmax + base;
-  uint32_t kv[kGather];
-  int32_t pv[kGather];
+  uint32_t kv[kFinGather];
+  int32_t pv[kFinGather];
 #pragma unroll
-  for (int u = 0; u < kGather; ++u) {
+  for (int u = 0; u < kFinGather; ++u) {
     const int e = min(sub + u * tpc, cap - 1);
     kv[u] = ck[e];
     pv[u] = cp[e];
   }
-  if (sel_from_hist) {  // the threshold bin of the finished histogram
+  const int n = visible(ctx_len, row, T, Lmax);
+  // (every load above has returned before the branch: otherwise the
+  // compiler moves the slice loads below it, after the context length)
+#pragma unroll
+  for (int u = 0; u < kFinGather; ++u) asm volatile("" ::"v"(kv[u]), "v"(pv[u]));
+  asm volatile("" ::"v"(cnt), "v"(hv[0]), "v"(hv[1]), "v"(hv[2]), "v"(hv[3]));
+  int32_t* out = idx + (int64_t)row * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    // the chunk kernels touched nothing for this row, but a fused
+    // histogram from the indexer may have
+    for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
+    return;
+  }
+  if (sel_from_hist) {  // the threshold bin of the finished histogram (one wave)
     *reinterpret_cast<i32x4*>(&sm.hist[4 * tid]) = hv;
     __syncthreads();
-    select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
-    b1 = sm.sel[0];
-    above1 = sm.sel[1];
+    if (tid < kWave) wave_select_bin<kBins1>(sm.hist, (uint32_t)k, sm.sel);
   }
   // ready for the next call (every thread's histogram load has returned)
   *reinterpret_cast<i32x4*>(hg + 4 * tid) = i32x4{0, 0, 0, 0};
@@ -537,7 +561,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     if (tid == 0) sm.chunk_off[n_chunks] = tot;
     if (sel_from_hist) listed = tot;  // every slice entry, extra ones included
   }
-  __syncthreads();
+  __syncthreads();  // (the scan's barriers also publish the selection)
+  if (sel_from_hist) {
+    b1 = sm.sel[0];
+    above1 = sm.sel[1];
+  }
   if (listed > (uint32_t)kTkCap) {
     if (scores != nullptr)
       finish_from_row(scores + (int64_t)row * ld, n, b1, above1, k, out, sm);
@@ -550,24 +578,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     const uint32_t off = sm.chunk_off[cq];
     const int cn = (int)(sm.chunk_off[cq + 1] - off);
 #pragma unroll
-    for (int u = 0; u < kGather; ++u) {
+    for (int u = 0; u < kFinGather; ++u) {
       const int e = sub + u * tpc;
       if (e < cn) {
         sm.list_key[off + e] = kv[u];
         sm.list_pos[off + e] = pv[u];
       }
     }
-    // the rest (long slices), batches of kGather entries per thread with
+    // the rest (long slices), batches of kFinGather entries per thread with
     // all loads issued first
-    for (int e0 = sub + kGather * tpc; e0 < cn; e0 += kGather * tpc) {
+    for (int e0 = sub + kFinGather * tpc; e0 < cn; e0 += kFinGather * tpc) {
 #pragma unroll
-      for (int u = 0; u < kGather; ++u) {
+      for (int u = 0; u < kFinGather; ++u) {
         const int e = min(e0 + u * tpc, cn - 1);
         kv[u] = ck[e];
         pv[u] = cp[e];
       }
 #pragma unroll
-      for (int u = 0; u < kGather; ++u) {
+      for (int u = 0; u < kFinGather; ++u) {
         const int e = e0 + u * tpc;
         if (e < cn) {
           sm.list_key[off + e] = kv[u];
@@ -576,8 +604,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
       }
     }
   }
+  // the second- and third-digit histograms, cleared while the list is copied
+  for (int i = tid; i < 2 * kBins2; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
-  finish_from_list((int)listed, b1, above1, k, out, sm);
+  finish_from_list((int)listed, b1, above1, k, out, sm, /*zeroed=*/true);
 }
 
 // Top-k per row among a position-ordered candidate list that holds every
@@ -630,7 +660,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_cand_kernel(
     for (int e = tid; e < M; e += kTkThreads) atomicAdd(&sm.hist[ck[e] >> 20], 1u);
   }
   __syncthreads();
-  select_bin<kBins1, kTkThreads>(sm.hist, (uint32_t)k, sm.scan, sm.sel);
+  if (tid < kWave) wave_select_bin<kBins1>(sm.hist, (uint32_t)k, sm.sel);
+  __syncthreads();
   const uint32_t b1 = sm.sel[0];
   const uint32_t above1 = sm.sel[1];
   __syncthreads();
@@ -758,9 +789,9 @@ hipError_t launch_topk_finish(const float* scores, int64_t ld, const int32_t* ct
   const size_t smem = sizeof(TopkSmem);
   hipError_t e = set_smem_attr((const void*)topk_finish_kernel, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(B * T), dim3(kTkThreads), smem, stream, scores, ld,
-                     ctx_len, T, Lmax, k, chunk, n_chunks, w.hist, w.key, w.pos, w.cnt, w.sel,
-                     sel_from_hist, idx);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(B * T), dim3(kTkThreads), smem, stream, w.hist,
+                     w.key, w.pos, w.cnt, ctx_len, T, Lmax, chunk, n_chunks, k, w.sel,
+                     (int)sel_from_hist, scores, ld, idx);
   return hipGetLastError();
 }
 
