@@ -25,12 +25,12 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 
-# Per-source extra flags.  The attention and top-k kernels have their first
-# 14 argument dwords preloaded into scalar registers at launch (gfx950
-# kernel-argument preloading; the code object keeps a fallback that loads
-# them itself), so their first loads wait on no argument load.
+# Per-source extra flags.  The decode indexer, attention and top-k kernels
+# have their first 14 argument dwords preloaded into scalar registers at
+# launch (gfx950 kernel-argument preloading; the code object keeps a fallback
+# that loads them itself), so their first loads wait on no argument load.
 _PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=14"]
-EXTRA = {"sparse_mla.hip": _PRELOAD, "topk.hip": _PRELOAD}
+EXTRA = {"sparse_mla.hip": _PRELOAD, "topk.hip": _PRELOAD, "indexer_decode.hip": _PRELOAD}
 
 
 def hipcc() -> str:

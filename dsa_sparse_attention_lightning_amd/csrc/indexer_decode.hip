@@ -85,12 +85,16 @@ struct FuseArgs {
   int32_t* pos;         // candidate positions, same layout
 };
 
+// The arguments the first loads depend on come first: the first 14 argument
+// dwords are preloaded into scalar registers at launch.  `plan` packs the
+// tiles per wave (low 16 bits) and the workgroups per row (high 16 bits),
+// which spares the first loads a wait for the grid size.
 template <int D, bool FP8, int HB, bool FUSE>
 __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
-    int Lmax, float* __restrict__ scores, int64_t ld, int tiles_per_wave,
+    const float* __restrict__ k_scale, int T, int H, int Lmax, int plan,
+    const int32_t* __restrict__ ctx_len, float* __restrict__ scores, int64_t ld,
     uint32_t* __restrict__ row_hist, FuseArgs fa) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int ROWB = D * EB;            // bytes per key row
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   const int g = lane >> 5;
   const int col = lane & 31;
   const int row = blockIdx.y;  // b * T + t
+  const int tiles_per_wave = plan & 0xffff;
   const int b = row / T;
   const int t = row - b * T;
   const int tiles = (Lmax + TK - 1) / TK;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   const int wg_end = FUSE ? min(tiles, (int)(blockIdx.x + 1) * kDecWaves * tiles_per_wave) : tiles;
   const int first = FUSE ? (int)blockIdx.x * kDecWaves * tiles_per_wave + wave
                          : (int)blockIdx.x * kDecWaves + wave;
-  const int wstride = FUSE ? kDecWaves : (int)gridDim.x * kDecWaves;
+  const int wstride = FUSE ? kDecWaves : (plan >> 16) * kDecWaves;
   const int tile0 = 0;
   // (a wave past the row's last tile runs no iteration but stays for the
   // workgroup barriers of the histogram)
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   auto tmap = [&](int j) { return __builtin_amdgcn_readfirstlane(first + j * wstride); };
   // fused: the tile after which a wave hands its bins off (none if < 0)
   const int hand_off = (3 * tend) / 4 - 1;
-  const int64_t pos = (int64_t)ctx_len[b] - T + t;
+  int64_t pos = 0;  // the row's position: read after the first loads are issued
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
   // Query fragments (operand A) and per-row head weights, through buffer
@@ -328,6 +333,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   load(tile0, ba, sa);
   load(tile0 + 1, bb, sb);
   __builtin_amdgcn_sched_barrier(0);  // then the first key tiles
+  pos = (int64_t)ctx_len[b] - T + t;  // (its argument is not preloaded: read it now)
   if (row_hist) {  // cleared while the first tiles stream in
     for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
     __syncthreads();
@@ -472,10 +478,11 @@ hipError_t launch_dec(const DecPlan& p, const void* q, const float* q_scale, con
                       const void* k, const float* k_scale, const int32_t* ctx_len, int rows,
                       int T, int H, int Lmax, float* scores, int64_t ld, uint32_t* row_hist,
                       const FuseArgs& fa, hipStream_t stream) {
+  if (p.tpw >= (1 << 16) || p.gx >= (1 << 15)) return hipErrorInvalidValue;  // plan packing
   dim3 grid(p.gx, rows);
   hipLaunchKernelGGL((indexer_decode_kernel<D, FP8, HB, FUSE>), grid, dim3(kDecWaves * kWave), 0,
-                     stream, (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, ctx_len,
-                     T, H, Lmax, scores, ld, p.tpw, row_hist, fa);
+                     stream, (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, T, H,
+                     Lmax, p.tpw | (p.gx << 16), ctx_len, scores, ld, row_hist, fa);
   return hipGetLastError();
 }
 
