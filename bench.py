@@ -134,7 +134,7 @@ def recorded_traffic(kernel: str, source: str):
     since the counters were taken."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", "decode_c3_traffic_pmc.md")
+    prof = os.path.join(ROOT, "profiles", "long_context_decode_traffic_pmc.md")
     src = os.path.join(ROOT, "dsa_sparse_attention_lightning_amd", "csrc", source)
     try:
         text = open(prof).read()
