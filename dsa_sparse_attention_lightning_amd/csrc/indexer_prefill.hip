@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
   constexpr int NV = HALF / 16;         // 16-byte vectors per lane per key
   constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
   constexpr int CH = kPfTile * CPR / kPfThreads;  // staged chunks per thread
+  constexpr bool kPipe = !FP8 && !FUSE;  // software-pipelined sub-blocks
   static_assert(CH >= 1 && kPfTile * CPR % kPfThreads == 0, "tile staging");
   __shared__ __align__(16) uint8_t ks[2][kPfTile * PITCH];
   __shared__ float kss[2][kPfTile];
@@ -227,20 +228,110 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
 
   gload(0);
   lstore(0);
+  // Every prologue load (query block, head weights) lands before the tile
+  // loop.  Left in flight, the compiler's wait counts carry them into the
+  // loop, where the first epilogue then waits vmcnt(3..0) on each pass: that
+  // wait also covers the next tile's key loads issued just before it, so
+  // their whole latency would show once per tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt untouched
   __syncthreads();
+  if constexpr (kPipe) {
+    // bf16, two waves per SIMD: software-pipelined sub-blocks.  The products
+    // of the next sub-block are issued one at a time between the epilogue
+    // steps of the current one (two accumulator values per product), so a
+    // wave keeps the matrix core busy through its own epilogue instead of
+    // leaving it to the SIMD's other wave; a tile's last epilogue runs under
+    // the first products of the next tile, after the tile barrier.  Every
+    // sub-block of a tile is computed; keys past kc store nothing.
+    constexpr int NP = NV * HB;      // products per sub-block
+    constexpr int NE = HB * 16 / 2;  // epilogue steps, two values each
+    constexpr int NS = kPfTile / 32; // sub-blocks per tile
+    static_assert(NS % 2 == 0, "a tile's last products land in the second accumulator");
+    auto read_b = [&](int buf, int sb, i32x4(&bv)[NV]) {
+      const uint8_t* bp = &ks[buf][(sb * 32 + col) * PITCH + g * HALF];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) bv[v] = *reinterpret_cast<const i32x4*>(bp + 16 * v);
+    };
+    auto prod = [&](int i, const i32x4(&bv)[NV], f32x16(&acc)[HB]) {
+      const int s = i / HB, hb = i % HB;
+      acc[hb] = mfma32_bf16(as_bf16x8(qv[hb][s]), as_bf16x8(bv[s]), s == 0 ? f32x16{} : acc[hb]);
+    };
+    auto step = [&](int e, const f32x16(&acc)[HB], float(&part)[kParts]) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int v = 2 * e + j, hb = v / 16, r = v % 16;
+        const float x = __int_as_float(max(__float_as_int(acc[hb][r]), 0));
+        part[v % kParts] = fmaf(wv[hb][r], x, part[v % kParts]);
+      }
+    };
+    auto finish = [&](int kbase, const float(&part)[kParts]) {
+      float sc = part[0];
+#pragma unroll
+      for (int p = 1; p < kParts; ++p) sc += part[p];
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false,
+                                                 false);
+      sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int key = kbase + col;
+      const bool st = g == 0 && live && key < kc;
+      const float o = key <= pos ? sc : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr,
+                                            (uint32_t)(st ? key : Lmax) * 4u, 0, 0);
+    };
+    // Epilogue of cur (keys kbase ..) with the products of bv into nxt.
+    auto overlap = [&](int kbase, const f32x16(&cur)[HB], const i32x4(&bv)[NV],
+                       f32x16(&nxt)[HB]) {
+      float part[kParts] = {};
+      step(0, cur, part);
+      step(1, cur, part);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        prod(i, bv, nxt);
+        if (i + 2 < NE) step(i + 2, cur, part);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = NP + 2; e < NE; ++e) step(e, cur, part);
+      finish(kbase, part);
+    };
+    f32x16 acc0[HB], acc1[HB];
+    i32x4 bv[NV];
+    read_b(0, 0, bv);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) prod(i, bv, acc0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int buf = tile & 1;
+      const bool more = tile + 1 < ntiles;
+      if (more) gload(tile + 1);
+      const int tbase = k0 + tile * kPfTile;
+#pragma unroll
+      for (int sb = 0; sb + 1 < NS; ++sb) {
+        read_b(buf, sb + 1, bv);
+        overlap(tbase + 32 * sb, (sb & 1) ? acc1 : acc0, bv, (sb & 1) ? acc0 : acc1);
+      }
+      if (more) {
+        lstore(buf ^ 1);
+        __syncthreads();
+        read_b(buf ^ 1, 0, bv);
+        overlap(tbase + 32 * (NS - 1), acc1, bv, acc0);
+      } else {
+        float part[kParts] = {};
+#pragma unroll
+        for (int e = 0; e < NE; ++e) step(e, acc1, part);
+        finish(tbase + 32 * (NS - 1), part);
+      }
+    }
+  } else {
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     if (tile + 1 < ntiles) gload(tile + 1);
     const int tbase = k0 + tile * kPfTile;
-#pragma unroll
-    for (int sb = 0; sb < kPfTile / 32; ++sb) {
-      const int kbase = tbase + sb * 32;
-      if (kbase >= kc) break;
+    // Products of sub-block sb (32 keys x the wave's heads) into acc.
+    auto mma = [&](int sb, f32x16(&acc)[HB]) {
       const uint8_t* bp = &ks[buf][(sb * 32 + col) * PITCH + g * HALF];
       i32x4 bv[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) bv[v] = *reinterpret_cast<const i32x4*>(bp + 16 * v);
-      f32x16 acc[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16{};
       if constexpr (!FP8) {
@@ -264,9 +355,13 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
           }
         }
       }
-      // ReLU as a signed-integer max on the bit pattern (negative floats,
-      // -0 included, have negative patterns), head sum in kParts chains,
-      // the other 16 rows of each head block from lane l ^ 32.
+    };
+    // Fused epilogue of sub-block sb.  ReLU as a signed-integer max on the
+    // bit pattern (negative floats, -0 included, have negative patterns),
+    // head sum in kParts chains, the other 16 rows of each head block from
+    // lane l ^ 32.
+    auto epi = [&](int sb, const f32x16(&acc)[HB]) {
+      const int kbase = tbase + sb * 32;
       float part[kParts];
 #pragma unroll
       for (int p = 0; p < kParts; ++p) part[p] = 0.f;
@@ -303,10 +398,22 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
           cpr[at] = key;
         }
         wcount += (uint32_t)__popcll(m);
-      } else if (g == 0 && live && key < kc) {
+      } else {
+        // One store per lane, no branch: a lane with nothing to store (the
+        // upper half-wave, an idle wave, a key past kc) points past the row,
+        // where the buffer's range check drops the store.
+        const bool st = g == 0 && live && key < kc;
         const float o = key <= pos ? (FP8 ? sc * kss[buf][sb * 32 + col] : sc) : -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, key * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr,
+                                              (uint32_t)(st ? key : Lmax) * 4u, 0, 0);
       }
+    };
+#pragma unroll
+    for (int sb = 0; sb < kPfTile / 32; ++sb) {
+      if (tbase + sb * 32 >= kc) break;
+      f32x16 acc[HB];
+      mma(sb, acc);
+      epi(sb, acc);
     }
     if constexpr (FUSE) {  // tighten the bound every 4 tiles (its own lanes' adds are done)
       if ((tile & 3) == 3) {
@@ -325,6 +432,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
+  }
   }
   if constexpr (FUSE) {
     if (live && lane == 0) fa.cnt[row] = wcount;
