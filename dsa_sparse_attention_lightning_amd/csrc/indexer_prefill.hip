@@ -8,7 +8,7 @@
 //
 //   * a workgroup holds 8 queries, one per wave; a wave keeps its query's
 //     [64 heads x D] block in registers (operand A of 32x32 MFMAs);
-//   * key tiles of 128 rows are staged through LDS (double-buffered, rows
+//   * key tiles of 128 or 256 rows are staged through LDS (double-buffered, rows
 //     padded by 16 bytes so the 32 lanes of a fragment read hit distinct
 //     banks) and shared by the 8 waves: operand B, 32 keys per MFMA column
 //     block;
@@ -40,7 +40,10 @@ namespace {
 
 constexpr int kPfWaves = 8;    // queries per workgroup
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfTile = 128;   // keys per LDS tile
+// Keys per LDS tile: 256 for the bf16 score kernel (one workgroup per CU
+// either way; half the tile barriers, measured 1% faster), 128 where two
+// workgroups share a CU (fp8) or the histograms need the room (fused).
+__host__ __device__ constexpr int pf_tile(bool fp8, bool fuse) { return (!fp8 && !fuse) ? 256 : 128; }
 constexpr int kParts = 4;      // independent fma chains of the head sum
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
@@ -112,17 +115,18 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ ctx_len, int T, int H,
     int Lmax, float* __restrict__ scores, int64_t ld, int keys_per_wg, PfFuseArgs fa) {
+  constexpr int TILE = pf_tile(FP8, FUSE);
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int ROWB = D * EB;          // bytes per key row
   constexpr int PITCH = ROWB + 16;      // LDS row pitch
   constexpr int HALF = ROWB / 2;        // bytes of a row per lane
   constexpr int NV = HALF / 16;         // 16-byte vectors per lane per key
   constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
-  constexpr int CH = kPfTile * CPR / kPfThreads;  // staged chunks per thread
+  constexpr int CH = TILE * CPR / kPfThreads;  // staged chunks per thread
   constexpr bool kPipe = !FP8 && !FUSE;  // software-pipelined sub-blocks
-  static_assert(CH >= 1 && kPfTile * CPR % kPfThreads == 0, "tile staging");
-  __shared__ __align__(16) uint8_t ks[2][kPfTile * PITCH];
-  __shared__ float kss[2][kPfTile];
+  static_assert(CH >= 1 && TILE * CPR % kPfThreads == 0, "tile staging");
+  __shared__ __align__(16) uint8_t ks[2][TILE * PITCH];
+  __shared__ float kss[2][TILE];
   __shared__ uint32_t whist[FUSE ? kPfWaves * kPfHistWords : 1];  // fused: per-wave histograms
 
   const int tid = threadIdx.x;
@@ -202,18 +206,18 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
       (void*)(FP8 ? k_scale + (int64_t)b * Lmax : k_scale), 0, FP8 ? Lmax * 4 : 0, kBufferWord3);
   const __amdgpu_buffer_rsrc_t outr =
       __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, FUSE ? 0 : Lmax * 4, kBufferWord3);
-  const int ntiles = (kc - k0 + kPfTile - 1) / kPfTile;
+  const int ntiles = (kc - k0 + TILE - 1) / TILE;
 
   i32x4 stage[CH];
   float stage_s = 1.f;
   auto gload = [&](int tile) {
-    const int base = __builtin_amdgcn_readfirstlane(k0 + tile * kPfTile);
+    const int base = __builtin_amdgcn_readfirstlane(k0 + tile * TILE);
 #pragma unroll
     for (int c = 0; c < CH; ++c)
       stage[c] = __builtin_bit_cast(
           i32x4, __builtin_amdgcn_raw_buffer_load_b128(
                      kr, base * ROWB + (tid + c * kPfThreads) * 16, 0, 0));
-    if (FP8 && tid < kPfTile)
+    if (FP8 && tid < TILE)
       stage_s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                               sr, (base + tid) * 4, 0, 0));
   };
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
       const int chunk = tid + c * kPfThreads;
       *reinterpret_cast<i32x4*>(&ks[buf][(chunk / CPR) * PITCH + (chunk % CPR) * 16]) = stage[c];
     }
-    if (FP8 && tid < kPfTile) kss[buf][tid] = stage_s;
+    if (FP8 && tid < TILE) kss[buf][tid] = stage_s;
   };
 
   gload(0);
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     // sub-block of a tile is computed; keys past kc store nothing.
     constexpr int NP = NV * HB;      // products per sub-block
     constexpr int NE = HB * 16 / 2;  // epilogue steps, two values each
-    constexpr int NS = kPfTile / 32; // sub-blocks per tile
+    constexpr int NS = TILE / 32;    // sub-blocks per tile
     static_assert(NS % 2 == 0, "a tile's last products land in the second accumulator");
     auto read_b = [&](int buf, int sb, i32x4(&bv)[NV]) {
       const uint8_t* bp = &ks[buf][(sb * 32 + col) * PITCH + g * HALF];
@@ -281,17 +285,20 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     auto overlap = [&](int kbase, const f32x16(&cur)[HB], const i32x4(&bv)[NV],
                        f32x16(&nxt)[HB]) {
       float part[kParts] = {};
-      step(0, cur, part);
-      step(1, cur, part);
+      // One epilogue step ahead of the first product (measured: none, two,
+      // three and six ahead are 1-2% slower)
+      constexpr int PRE = 1;
+#pragma unroll
+      for (int e = 0; e < PRE; ++e) step(e, cur, part);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         prod(i, bv, nxt);
-        if (i + 2 < NE) step(i + 2, cur, part);
+        if (i + PRE < NE) step(i + PRE, cur, part);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int e = NP + 2; e < NE; ++e) step(e, cur, part);
+      for (int e = NP + PRE; e < NE; ++e) step(e, cur, part);
       finish(kbase, part);
     };
     f32x16 acc0[HB], acc1[HB];
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
       const int buf = tile & 1;
       const bool more = tile + 1 < ntiles;
       if (more) gload(tile + 1);
-      const int tbase = k0 + tile * kPfTile;
+      const int tbase = k0 + tile * TILE;
 #pragma unroll
       for (int sb = 0; sb + 1 < NS; ++sb) {
         read_b(buf, sb + 1, bv);
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     if (tile + 1 < ntiles) gload(tile + 1);
-    const int tbase = k0 + tile * kPfTile;
+    const int tbase = k0 + tile * TILE;
     // Products of sub-block sb (32 keys x the wave's heads) into acc.
     auto mma = [&](int sb, f32x16(&acc)[HB]) {
       const uint8_t* bp = &ks[buf][(sb * 32 + col) * PITCH + g * HALF];
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
       }
     };
 #pragma unroll
-    for (int sb = 0; sb < kPfTile / 32; ++sb) {
+    for (int sb = 0; sb < TILE / 32; ++sb) {
       if (tbase + sb * 32 >= kc) break;
       f32x16 acc[HB];
       mma(sb, acc);
@@ -444,14 +451,15 @@ hipError_t launch_pf(const void* q, const float* q_scale, const float* w, const 
                      const float* k_scale, const int32_t* ctx_len, int B, int T, int H, int Lmax,
                      float* scores, int64_t ld, const PfFuseArgs& fa, hipStream_t stream) {
   const int qgroups = (T + kPfWaves - 1) / kPfWaves;
-  const int tiles = (Lmax + kPfTile - 1) / kPfTile;
+  constexpr int TILE = pf_tile(FP8, FUSE);
+  const int tiles = (Lmax + TILE - 1) / TILE;
   // Split the keys so the grid holds >= ~8 workgroups per CU (the fused
   // variant keeps each row in one workgroup).
   int splits = (2048 + qgroups * B - 1) / (qgroups * B);
   splits = max(splits, 8);
   splits = FUSE ? 1 : max(1, min(splits, tiles));
   const int tiles_per = (tiles + splits - 1) / splits;
-  const int keys_per_wg = tiles_per * kPfTile;
+  const int keys_per_wg = tiles_per * TILE;
   const dim3 grid(qgroups, (Lmax + keys_per_wg - 1) / keys_per_wg, B);
   hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D, HB, FUSE>), grid, dim3(kPfThreads), 0,
                      stream, (const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, ctx_len,
