@@ -142,18 +142,23 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   int64_t pos = 0;  // the row's position: read after the first loads are issued
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
-  // Query fragments (operand A) and per-row head weights, through buffer
-  // resources over this row: every load is unconditional (a head past H reads
-  // zeros and adds nothing), so all of a wave's prologue loads are in flight
-  // together.  They are issued before the first key tiles and their products
-  // w * q_scale are formed after those tiles are requested: the memory counter
-  // completes in order, so that wait covers these loads only and the key
-  // stream starts at once.  (Written with a branch per head, the compiler
-  // waited for each weight in turn before the first key load, and the stream
-  // started 5 to 14 us into the launch.)
-  i32x4 qv[HB][NV];
-  float wv[HB][16];
-  float qsv[FP8 ? HB : 1][16];
+  // The row's query block, head weights and query scales are the same for
+  // all eight waves, so they are loaded once per workgroup and shared
+  // through LDS: each thread loads one 16-byte share of the (zero-padded)
+  // query block and every wave one weight and one scale per lane, through
+  // buffer resources over this row (a head past H reads zeros and adds
+  // nothing).  These few loads go out ahead of the first key tiles, whose
+  // requests then do not queue behind 8 copies of the same prologue loads
+  // (24 per wave: the first tiles were issued 5 us into the launch at the
+  // median, 13 us for the last waves); the memory counter completes in
+  // order, so waiting for these loads does not wait for the tiles.
+  constexpr int QPITCH = ROWB + 16;                     // LDS row pitch of the query block
+  constexpr int QCH = HB * 32 * ROWB / 16;              // 16-byte chunks of the block
+  constexpr int QPT = (QCH + kDecWaves * kWave - 1) / (kDecWaves * kWave);  // per thread
+  __shared__ __align__(16) unsigned char qsh[HB * 32 * QPITCH];
+  __shared__ __align__(16) float wsh[HB * 32];
+  i32x4 qld[QPT];
+  float wl, ql;
   {
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(q + (int64_t)row * H * ROWB), 0, H * ROWB, kBufferWord3);
@@ -162,50 +167,43 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
     const __amdgpu_buffer_rsrc_t qsr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(FP8 ? q_scale + (int64_t)row * H : w), 0, FP8 ? H * 4 : 0, kBufferWord3);
 #pragma unroll
+    for (int u = 0; u < QPT; ++u)
+      qld[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             qr, (threadIdx.x + kDecWaves * kWave * u) * 16, 0, 0));
+    wl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, lane * 4, 0, 0));
+    ql = FP8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qsr, lane * 4, 0, 0))
+             : 1.f;
+  }
+  // Operand A fragments and head weights of this wave, from LDS after the
+  // prologue barrier.
+  i32x4 qv[HB][NV];
+  float wv[HB][16];
+  auto share_prologue = [&]() {  // before the barrier
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int c = threadIdx.x + kDecWaves * kWave * u;
+      if (c < QCH)
+        *reinterpret_cast<i32x4*>(qsh + (c / (ROWB / 16)) * QPITCH + (c % (ROWB / 16)) * 16) =
+            qld[u];
+    }
+    // w' = w (bf16) or w * q_scale (fp8: the positive per-row scales commute
+    // with the ReLU)
+    if (wave == 0 && lane < HB * 32) wsh[lane] = wl * ql;
+  };
+  auto take_prologue = [&]() {  // after the barrier
+#pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      const int head = hb * 32 + col;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
-        qv[hb][v] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  qr, head * ROWB + g * HALF + 16 * v, 0, 0));
-      // Accumulator rows r = 4j .. 4j+3 are heads hb*32 + 8j + 4g + 0..3: four
-      // consecutive weights per 16-byte load when H is a multiple of 4 (a
-      // 16-byte load straddling the end of the range would read as zero
-      // whole); otherwise one load per weight.
-      if (H % 4 == 0) {
+        qv[hb][v] = *reinterpret_cast<const i32x4*>(qsh + (hb * 32 + col) * QPITCH + g * HALF +
+                                                    16 * v);
+      // Accumulator rows r = 4j .. 4j+3 are heads hb*32 + 8j + 4g + 0..3.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h0 = hb * 32 + 8 * j + 4 * g;
-          const f32x4 wq =
-              __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, h0 * 4, 0, 0));
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 wq = *reinterpret_cast<const f32x4*>(wsh + hb * 32 + 8 * j + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wv[hb][4 * j + e] = wq[e];
-          if constexpr (FP8) {
-            const f32x4 sq =
-                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qsr, h0 * 4, 0, 0));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) qsv[hb][4 * j + e] = sq[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int h = hb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          wv[hb][r] =
-              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, h * 4, 0, 0));
-          if constexpr (FP8)
-            qsv[hb][r] =
-                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qsr, h * 4, 0, 0));
-        }
+        for (int e = 0; e < 4; ++e) wv[hb][4 * j + e] = wq[e];
       }
-    }
-  }
-  auto fold_scales = [&]() {
-    if constexpr (FP8) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) wv[hb][r] *= qsv[hb][r];
     }
   };
 
@@ -334,11 +332,11 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
   load(tile0 + 1, bb, sb);
   __builtin_amdgcn_sched_barrier(0);  // then the first key tiles
   pos = (int64_t)ctx_len[b] - T + t;  // (its argument is not preloaded: read it now)
-  if (row_hist) {  // cleared while the first tiles stream in
+  share_prologue();
+  if (row_hist)  // cleared while the first tiles stream in
     for (int i = threadIdx.x; i < kHistBins; i += kDecWaves * kWave) lhist[i] = 0;
-    __syncthreads();
-  }
-  fold_scales();
+  __syncthreads();
+  take_prologue();
   // Whole rounds of three tiles, then the zero to two left over: the loop has
   // no exit in its body, so no path into its head skips a round's loads.
   int tile = tile0;
