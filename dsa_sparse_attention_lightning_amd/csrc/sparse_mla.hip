@@ -589,7 +589,9 @@ constexpr int kCombHeads = 2;
 __global__ __launch_bounds__(kCombHeads * 64) void sparse_mla_combine_kernel(
     const __bf16* __restrict__ part_o, const float* __restrict__ part_lse, int Hq, int n_split,
     __bf16* __restrict__ out, float* __restrict__ lse) {
-  const int head = blockIdx.y * kCombHeads + threadIdx.x / 64;
+  // (wave-uniform: the 16 per-split log-sum-exps of the wave's head are then
+  // scalar loads rather than 16 vector loads per lane of the same address)
+  const int head = __builtin_amdgcn_readfirstlane(blockIdx.y * kCombHeads + threadIdx.x / 64);
   if (head >= Hq) return;
   combine_unit(part_o, part_lse, Hq, n_split, blockIdx.x, head, (threadIdx.x & 63) * 8, out,
                lse, (threadIdx.x & 63) == 0);
