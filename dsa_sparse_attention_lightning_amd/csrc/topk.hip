@@ -304,6 +304,110 @@ __device__ __forceinline__ int visible(const int32_t* ctx_len, int row, int T, i
   return (int)max((int64_t)0, min(pos + 1, (int64_t)Lmax));
 }
 
+// A row of at most kRegRow scores held in registers (64 per thread), so it is
+// read once, in one round trip: batch b of 16384 positions gives thread t
+// positions 16384 b + 16 t .. + 15.  The first-digit histogram is counted
+// from the registers, and the candidates (bins >= b1) are copied into the
+// LDS list in position order from the same registers: one prefix scan of
+// the four batches' per-thread counts (two 16-bit fields per word) places
+// every thread's run.  (Reading the row twice, a batch in flight at a time,
+// took 15 + 11 us per row of the 64K-context prefill chunk.)
+constexpr int kRegBatches = 4;
+constexpr int kRegRow = kRegBatches * 16 * kTkThreads;  // 65536
+__device__ __forceinline__ void row_in_registers(__amdgpu_buffer_rsrc_t r, int n, int k,
+                                                 int32_t* out, TopkSmem& sm, const float* src) {
+  const int tid = threadIdx.x;
+  uint32_t key[kRegBatches][16];
+#pragma unroll
+  for (int b = 0; b < kRegBatches; ++b)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(r, (16384 * b + 16 * tid + 4 * v) * 4, 0, 0));
+      key[b][4 * v] = float_key(x.x);
+      key[b][4 * v + 1] = float_key(x.y);
+      key[b][4 * v + 2] = float_key(x.z);
+      key[b][4 * v + 3] = float_key(x.w);
+    }
+  auto pos = [&](int b, int e) { return 16384 * b + 16 * tid + e; };
+  // Only the bins at and above the k-th largest key's matter, and counting
+  // every key piles the LDS atomics onto the few bins that hold the bulk of
+  // the row (13 us per row here).  So a lower bound L of that bin is taken
+  // first from a sample, one key per thread (positions 16 t): the bin of
+  // the sample's kSample-th largest key.  Only keys in bins >= L are then
+  // counted; if they number at least k, the k-th largest lies at or above L
+  // and the counts above it are exact, otherwise (a sample that ran high)
+  // every key is counted.  A row reaching this path has n > k; with fewer
+  // than kSample valid sample keys the bound is bin 0 (every key).
+  constexpr uint32_t kSample = 128;
+  static_assert(kSample <= (uint32_t)kTkThreads, "one sample key per thread");
+  const uint32_t valid = (uint32_t)min(kTkThreads, (n + 15) / 16);
+  for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
+  if (tid == 0) sm.sel[0] = 0;
+  __syncthreads();
+  if (pos(0, 0) < n) atomicAdd(&sm.hist[key[0][0] >> 20], 1u);
+  __syncthreads();
+  if (valid >= kSample && tid < kWave) wave_select_bin<kBins1>(sm.hist, kSample, sm.sel);
+  __syncthreads();
+  const uint32_t lb = sm.sel[0];
+  for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  uint32_t counted = 0;
+#pragma unroll
+  for (int b = 0; b < kRegBatches; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (pos(b, e) < n && (key[b][e] >> 20) >= lb) {
+        atomicAdd(&sm.hist[key[b][e] >> 20], 1u);
+        ++counted;
+      }
+  uint32_t total;
+  block_excl_scan<kTkWaves>(counted, sm.scan, total);  // (its barriers follow the adds)
+  if (total < (uint32_t)k) {  // the sample's bound ran above the k-th key: count them all
+#pragma unroll
+    for (int b = 0; b < kRegBatches; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (pos(b, e) < n && (key[b][e] >> 20) < lb) atomicAdd(&sm.hist[key[b][e] >> 20], 1u);
+    __syncthreads();
+  }
+  if (tid < kWave) wave_select_bin<kBins1>(sm.hist, (uint32_t)k, sm.sel);
+  __syncthreads();
+  const uint32_t b1 = sm.sel[0];
+  const uint32_t above1 = sm.sel[1];
+  const uint32_t listed = above1 + sm.hist[b1];
+  __syncthreads();
+  if (listed > (uint32_t)kTkCap) {
+    finish_from_row(src, n, b1, above1, k, out, sm);
+    return;
+  }
+  uint32_t c[kRegBatches];
+#pragma unroll
+  for (int b = 0; b < kRegBatches; ++b) {
+    c[b] = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[b] += (pos(b, e) < n && (key[b][e] >> 20) >= b1) ? 1u : 0u;
+  }
+  // per-batch totals stay below 65536 (16384 positions), so two batches
+  // share a word of 16-bit fields through the scan
+  uint32_t tot01, tot23;
+  const uint32_t ex01 = block_excl_scan<kTkWaves>(c[0] | (c[1] << 16), sm.scan, tot01);
+  const uint32_t ex23 = block_excl_scan<kTkWaves>(c[2] | (c[3] << 16), sm.scan, tot23);
+  const uint32_t t0 = tot01 & 0xffffu, t1 = tot01 >> 16, t2 = tot23 & 0xffffu;
+  uint32_t at[kRegBatches] = {ex01 & 0xffffu, t0 + (ex01 >> 16), t0 + t1 + (ex23 & 0xffffu),
+                              t0 + t1 + t2 + (ex23 >> 16)};
+#pragma unroll
+  for (int b = 0; b < kRegBatches; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (pos(b, e) < n && (key[b][e] >> 20) >= b1) {
+        sm.list_key[at[b]] = key[b][e];
+        sm.list_pos[at[b]] = pos(b, e);
+        ++at[b];
+      }
+  finish_from_list((int)listed, b1, above1, k, out, sm);  // (its first barrier publishes the list)
+}
+
 // ---------------------------------------------------------------- one workgroup per row
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ ctx_len, int T,
@@ -320,6 +424,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
   }
   const float* src = scores + (int64_t)row * ld;
   const __amdgpu_buffer_rsrc_t r = row_rsrc(src, n);
+  if (n <= kRegRow) {
+    row_in_registers(r, n, k, out, sm, src);
+    return;
+  }
   for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
   for_each_key(r, n, [&](uint32_t key) { atomicAdd(&sm.hist[key >> 20], 1u); });

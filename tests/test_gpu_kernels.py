@@ -85,6 +85,10 @@ def _rand_scores(B, T, L, seed, kind="normal"):
     g.manual_seed(seed)
     if kind == "normal":
         x = torch.randn((B, T, L), generator=g, device=DEV)
+    elif kind == "sampletop":  # every 16th position of the first 16384 far above the rest
+        x = torch.rand((B, T, L), generator=g, device=DEV)
+        m = min(1024, (L + 15) // 16)
+        x[..., 0:16 * m:16] = 10.0 + torch.arange(m, device=DEV, dtype=torch.float32) / 1000.0
     elif kind == "few":        # heavy ties: 7 distinct values
         x = torch.randint(0, 7, (B, T, L), generator=g, device=DEV).float()
     elif kind == "equal":
@@ -137,6 +141,14 @@ TOPK_CASES = [
     (1, 4, 8192, [8192], 2048, "cluster3000"),                   # row kernel (T > 1)
     (1, 4, 8192, [8192], 2048, "clustertie2200"),
     (1, 4, 8192, [8192], 1000, "cluster6000"),
+    # row kernel (more than 128 rows), rows held in registers (n <= 65536):
+    # a bin bound taken from one sampled key per thread (positions 16 t),
+    # which falls back to counting every key when the sample runs high
+    # ("sampletop": the sampled positions hold the largest scores); rows up
+    # to 65536, and rows on both sides of it
+    (1, 130, 60000, [60000], 2048, "sampletop"),
+    (1, 130, 65536, [65536], 2048, "normal"),
+    (1, 130, 65600, [65600], 2048, "normal"),
 ]
 
 
