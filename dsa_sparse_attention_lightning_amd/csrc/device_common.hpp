@@ -78,26 +78,35 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return (uint32_t)v;
 }
 
+// Inclusive prefix sum over lanes 0..15 (one DPP row); other lanes unused.
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return (uint32_t)v;
+}
+
 // Block-wide exclusive prefix sum of one value per thread.  `scratch` holds
 // NW words of LDS.  Returns the exclusive prefix; `total` gets the sum.
 // Contains two __syncthreads, so every thread of the block must call it.
+// The wave totals are scanned by every wave at once (lane i reads wave i's
+// total, one DPP row scan, two lane reads), so the cross-wave step costs a
+// handful of instructions per wave whatever NW is.
 template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch,
                                                     uint32_t& total) {
+  static_assert(NW >= 1 && NW <= 16, "wave totals fit one DPP row");
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   uint32_t incl = wave_incl_scan(v);
   if (lane == kWave - 1) scratch[wid] = incl;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    uint32_t t = scratch[i];
-    before += (i < wid) ? t : 0u;
-    tot += t;
-  }
+  const uint32_t ti = row16_incl_scan(lane < NW ? scratch[lane] : 0u);
+  const uint32_t before = wid > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)ti, wid - 1) : 0u;
+  total = (uint32_t)__builtin_amdgcn_readlane((int)ti, NW - 1);
   __syncthreads();
-  total = tot;
   return before + incl - v;
 }
 
@@ -152,11 +161,20 @@ __device__ void wave_select_bin(const uint32_t* hist, uint32_t kk, uint32_t* sel
   const int lane = threadIdx.x & (kWave - 1);
   const int lo = NB - PER * (lane + 1);
   uint32_t sum = 0;
+  if constexpr (V <= 4) {  // every read in flight before the first add
+    uint4 x[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int v = (i + lane) & (V - 1);
-    const uint4 x = *reinterpret_cast<const uint4*>(hist + lo + 4 * v);
-    sum += x.x + x.y + x.z + x.w;
+    for (int i = 0; i < V; ++i)
+      x[i] = *reinterpret_cast<const uint4*>(hist + lo + 4 * ((i + lane) & (V - 1)));
+#pragma unroll
+    for (int i = 0; i < V; ++i) sum += x[i].x + x[i].y + x[i].z + x[i].w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int v = (i + lane) & (V - 1);
+      const uint4 x = *reinterpret_cast<const uint4*>(hist + lo + 4 * v);
+      sum += x.x + x.y + x.z + x.w;
+    }
   }
   const uint32_t incl = wave_incl_scan(sum);
   const uint64_t m = __ballot(incl - sum < kk && kk <= incl);

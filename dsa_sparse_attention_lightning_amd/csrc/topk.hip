@@ -51,6 +51,7 @@ struct TopkSmem {
   uint32_t list_key[kTkCap];
   int32_t list_pos[kTkCap];
   uint32_t scan[kTkWaves];
+  uint32_t scan2[kTkWaves];
   uint32_t sel[4];
   uint32_t chunk_off[kMaxChunks + 1];
 };
@@ -200,6 +201,51 @@ __device__ __forceinline__ void finish_from_list(int M, uint32_t b1, uint32_t ab
                      p[4] = p1.x; p[5] = p1.y; p[6] = p1.z; p[7] = p1.w;
 #pragma unroll
                      for (int j = 0; j < 8; ++j) ok[j] = (e + j) < M;
+                   });
+}
+
+// Steps 3-4 for a list of at most 8 kTkThreads entries whose second-digit
+// histogram (sm.hist[0, 1024)) is already counted and whose third-digit one
+// (sm.hist[1024, 2048)) is zero: each thread reads its 8 consecutive entries
+// once, while one wave picks the second digit, and keeps them in registers
+// for the third digit and the ordered emission.
+__device__ __forceinline__ void finish_from_list_once(int M, uint32_t b1, uint32_t above1, int k,
+                                                      int32_t* out, TopkSmem& sm) {
+  const int tid = threadIdx.x;
+  uint32_t* h2 = sm.hist;
+  uint32_t* h3 = sm.hist + kBins2;
+  const int e0 = 8 * tid;
+  // (unconditional 16-byte reads: entries past M are stale and masked)
+  const uint4 k0 = *reinterpret_cast<const uint4*>(&sm.list_key[e0]);
+  const uint4 k1 = *reinterpret_cast<const uint4*>(&sm.list_key[e0 + 4]);
+  const int4 p0 = *reinterpret_cast<const int4*>(&sm.list_pos[e0]);
+  const int4 p1 = *reinterpret_cast<const int4*>(&sm.list_pos[e0 + 4]);
+  const uint32_t key[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+  const int32_t pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  bool ok[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ok[j] = e0 + j < M;
+  if (tid < kWave) wave_select_bin<kBins2>(h2, (uint32_t)k - above1, sm.sel);
+  __syncthreads();
+  const uint32_t b2 = sm.sel[0];
+  const uint32_t above2 = sm.sel[1];
+  const uint32_t pre2 = (b1 << 10) | b2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (ok[j] && (key[j] >> 10) == pre2) atomicAdd(&h3[key[j] & 1023u], 1u);
+  __syncthreads();
+  if (tid < kWave) wave_select_bin<kBins2>(h3, (uint32_t)k - above1 - above2, sm.sel + 2);
+  __syncthreads();
+  const uint32_t tau = (b1 << 20) | (b2 << 10) | sm.sel[2];
+  const uint32_t take_eq = (uint32_t)k - above1 - above2 - sm.sel[3];
+  emit_selected<8>(M, tau, take_eq, out, sm,
+                   [&](int, uint32_t(&kk)[8], int32_t(&pp)[8], bool(&oo)[8]) {
+#pragma unroll
+                     for (int j = 0; j < 8; ++j) {
+                       kk[j] = key[j];
+                       pp[j] = pos[j];
+                       oo[j] = ok[j];
+                     }
                    });
 }
 
@@ -644,7 +690,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
   // compiler moves the slice loads below it, after the context length)
 #pragma unroll
   for (int u = 0; u < kFinGather; ++u) asm volatile("" ::"v"(kv[u]), "v"(pv[u]));
-  asm volatile("" ::"v"(cnt), "v"(hv[0]), "v"(hv[1]), "v"(hv[2]), "v"(hv[3]));
+  asm volatile("" ::"v"(cnt), "v"(hv[0]), "v"(hv[1]), "v"(hv[2]), "v"(hv[3]), "v"(b1),
+               "v"(above1), "v"(listed));
   int32_t* out = idx + (int64_t)row * k;
   if (n <= k) {
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
@@ -653,23 +700,56 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
     for (int i = tid; i < kBins1; i += kTkThreads) hg[i] = 0;
     return;
   }
-  if (sel_from_hist) {  // the threshold bin of the finished histogram (one wave)
-    *reinterpret_cast<i32x4*>(&sm.hist[4 * tid]) = hv;
-    __syncthreads();
-    if (tid < kWave) wave_select_bin<kBins1>(sm.hist, (uint32_t)k, sm.sel);
-  }
-  // ready for the next call (every thread's histogram load has returned)
-  *reinterpret_cast<i32x4*>(hg + 4 * tid) = i32x4{0, 0, 0, 0};
-  // concatenate the chunk slices in chunk order: prefix sum of the slice
-  // counts, then each slice is copied by its own group of tpc threads
+  // The second- and third-digit histograms start at zero (cleared now, in
+  // LDS that nothing else uses before the list is complete).
+  for (int i = tid; i < 2 * kBins2; i += kTkThreads) sm.hist[i] = 0;
+  // One block-wide scan of two values per thread: the slice counts (their
+  // exclusive prefix places each slice in the list) and, after the fused
+  // indexer, the sums of this thread's four histogram bins (4 tid .. 4 tid
+  // + 3), whose inclusive prefix gives the count above each bin.
   {
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<kTkWaves>(cnt, sm.scan, tot);
-    if (tid < n_chunks) sm.chunk_off[tid] = ex;
-    if (tid == 0) sm.chunk_off[n_chunks] = tot;
-    if (sel_from_hist) listed = tot;  // every slice entry, extra ones included
+    const int lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t hs = sel_from_hist ? (uint32_t)(hv[0] + hv[1] + hv[2] + hv[3]) : 0u;
+    const uint32_t hin = wave_incl_scan(hs);
+    const uint32_t cin = wave_incl_scan(cnt);
+    if (lane == kWave - 1) {
+      sm.scan[wid] = hin;
+      sm.scan2[wid] = cin;
+    }
+    if (tid == 0) {  // (overwritten after the barrier by the bin's thread)
+      sm.sel[0] = 0;
+      sm.sel[1] = 0;
+    }
+    // ready for the next call (every thread's histogram load has returned)
+    *reinterpret_cast<i32x4*>(hg + 4 * tid) = i32x4{0, 0, 0, 0};
+    __syncthreads();
+    // (lane i scans wave i's totals; the wave reads its own prefix back)
+    const uint32_t hw = row16_incl_scan(lane < kTkWaves ? sm.scan[lane] : 0u);
+    const uint32_t cw = row16_incl_scan(lane < kTkWaves ? sm.scan2[lane] : 0u);
+    const uint32_t htot = (uint32_t)__builtin_amdgcn_readlane((int)hw, kTkWaves - 1);
+    const uint32_t ctot = (uint32_t)__builtin_amdgcn_readlane((int)cw, kTkWaves - 1);
+    const uint32_t hbefore = wid > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)hw, wid - 1) : 0u;
+    const uint32_t cbefore = wid > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)cw, wid - 1) : 0u;
+    if (tid < n_chunks) sm.chunk_off[tid] = cbefore + cin - cnt;
+    if (tid == 0) sm.chunk_off[n_chunks] = ctot;
+    if (sel_from_hist) {
+      // exactly one bin holds the k-th largest key (the histogram counts
+      // every visible key and n > k): its thread records it
+      uint32_t above = htot - (hbefore + hin);
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const uint32_t c = (uint32_t)hv[j];
+        if (above < (uint32_t)k && (uint32_t)k <= above + c) {
+          sm.sel[0] = 4 * tid + j;
+          sm.sel[1] = above;
+        }
+        above += c;
+      }
+      listed = ctot;  // every slice entry, extra ones included
+    }
+    __syncthreads();
   }
-  __syncthreads();  // (the scan's barriers also publish the selection)
   if (sel_from_hist) {
     b1 = sm.sel[0];
     above1 = sm.sel[1];
@@ -682,6 +762,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
                          n_chunks, (int)listed, b1, above1, k, out, sm);
     return;
   }
+  // A list that one emission pass covers has its second-digit histogram
+  // counted here, from the registers, while it is copied.
+  const bool count2 = listed <= (uint32_t)(8 * kTkThreads);
+  uint32_t* h2 = sm.hist;
   if (cq < n_chunks) {
     const uint32_t off = sm.chunk_off[cq];
     const int cn = (int)(sm.chunk_off[cq + 1] - off);
@@ -691,6 +775,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
       if (e < cn) {
         sm.list_key[off + e] = kv[u];
         sm.list_pos[off + e] = pv[u];
+        if (count2 && (kv[u] >> 20) == b1) atomicAdd(&h2[(kv[u] >> 10) & 1023u], 1u);
       }
     }
     // the rest (long slices), batches of kFinGather entries per thread with
@@ -708,14 +793,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(
         if (e < cn) {
           sm.list_key[off + e] = kv[u];
           sm.list_pos[off + e] = pv[u];
+          if (count2 && (kv[u] >> 20) == b1) atomicAdd(&h2[(kv[u] >> 10) & 1023u], 1u);
         }
       }
     }
   }
-  // the second- and third-digit histograms, cleared while the list is copied
-  for (int i = tid; i < 2 * kBins2; i += kTkThreads) sm.hist[i] = 0;
   __syncthreads();
-  finish_from_list((int)listed, b1, above1, k, out, sm, /*zeroed=*/true);
+  if (!count2) {
+    finish_from_list((int)listed, b1, above1, k, out, sm, /*zeroed=*/true);
+    return;
+  }
+  finish_from_list_once((int)listed, b1, above1, k, out, sm);
 }
 
 // Top-k per row among a position-ordered candidate list that holds every
