@@ -138,6 +138,8 @@ TOPK_CASES = [
     (2, 1, 40000, [40000, 39000], 2048, "cluster2500"),          # chunked rows
     (2, 1, 40000, [40000, 39000], 2048, "clustertie3072"),
     (2, 1, 40000, [40000, 39000], 2048, "cluster5000"),
+    # a list longer than one emission pass (8192 entries) but inside LDS
+    (2, 1, 40000, [40000, 39000], 2048, "cluster11000"),
     (1, 4, 8192, [8192], 2048, "cluster3000"),                   # row kernel (T > 1)
     (1, 4, 8192, [8192], 2048, "clustertie2200"),
     (1, 4, 8192, [8192], 1000, "cluster6000"),
