@@ -254,6 +254,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       *reinterpret_cast<i32x4*>(my_stage + (off / ROWB) * PITCH + (off % ROWB)) = raw[v];
     }
     __builtin_amdgcn_wave_barrier();
+    float scs[CB];  // per-lane head sums of each block (even CB)
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       i32x4 cur[NV];
@@ -298,19 +299,41 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       float sc = part[0];
 #pragma unroll
       for (int p = 1; p < kParts; ++p) sc += part[p];
-      {
+      if constexpr (CB % 2 == 0) {
+        scs[c] = sc;  // (the two lane halves are added below, two blocks at a time)
+      } else {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc),
                                                    false, false);
         sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int key = tile * TK + c * 32 + col;
+        const bool vis = key <= pos && key < Lmax;
+        const float o = vis ? (FP8 ? sc * cs[c] : sc) : -INFINITY;
+        if constexpr (!FUSE)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr,
+                                                (key + (g ? kPastEnd : 0)) * 4, 0, 0);
+        if (g == 0) {
+          if constexpr (FUSE) sbuf[(seq * kDecWaves + wave) * TK + c * 32 + col] = o;
+          if (row_hist && vis) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);
+        }
       }
-      const int key = tile * TK + c * 32 + col;
-      const bool vis = key <= pos && key < Lmax;
-      const float o = vis ? (FP8 ? sc * cs[c] : sc) : -INFINITY;
-      if constexpr (!FUSE)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr,
-                                              (key + (g ? kPastEnd : 0)) * 4, 0, 0);
-      if (g == 0) {
-        if constexpr (FUSE) sbuf[(seq * kDecWaves + wave) * TK + c * 32 + col] = o;
+    }
+    if constexpr (CB % 2 == 0) {
+      // Blocks c and c + 1 in one lane swap: the swap exchanges the upper
+      // half of its first operand with the lower half of its second, so the
+      // sum of the two results holds block c's scores in lanes 0..31 and
+      // block c + 1's in lanes 32..63, i.e. key c * 32 + lane, and one store
+      // of 64 consecutive scores writes both.
+#pragma unroll
+      for (int c = 0; c < CB; c += 2) {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(scs[c]),
+                                                   __float_as_uint(scs[c + 1]), false, false);
+        const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int key = tile * TK + c * 32 + lane;
+        const bool vis = key <= pos && key < Lmax;
+        const float o = vis ? (FP8 ? sc * (g ? cs[c + 1] : cs[c]) : sc) : -INFINITY;
+        if constexpr (!FUSE)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), outr, key * 4, 0, 0);
+        if constexpr (FUSE) sbuf[(seq * kDecWaves + wave) * TK + c * 32 + lane] = o;
         if (row_hist && vis) atomicAdd(&lhist[float_key(o) >> (32 - kHistBits)], 1u);
       }
     }
