@@ -118,12 +118,15 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
   constexpr int TILE = pf_tile(FP8, FUSE);
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int ROWB = D * EB;          // bytes per key row
-  constexpr int PITCH = ROWB + 16;      // LDS row pitch
+  constexpr bool kPipe = !FUSE && !FP8;  // software-pipelined sub-blocks (bf16)
+  // LDS row pitch: padded rows for the register-staged tiles; the pipelined
+  // kernel's tiles arrive by LDS-DMA, unpadded, with each row's 16-byte
+  // chunks permuted instead (chunk c of row r at position c ^ (r % CPR)).
+  constexpr int PITCH = kPipe ? ROWB : ROWB + 16;
   constexpr int HALF = ROWB / 2;        // bytes of a row per lane
   constexpr int NV = HALF / 16;         // 16-byte vectors per lane per key
   constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
   constexpr int CH = TILE * CPR / kPfThreads;  // staged chunks per thread
-  constexpr bool kPipe = !FP8 && !FUSE;  // software-pipelined sub-blocks
   static_assert(CH >= 1 && TILE * CPR % kPfThreads == 0, "tile staging");
   __shared__ __align__(16) uint8_t ks[2][TILE * PITCH];
   __shared__ float kss[2][TILE];
@@ -230,8 +233,29 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     if (FP8 && tid < TILE) kss[buf][tid] = stage_s;
   };
 
-  gload(0);
-  lstore(0);
+  // The next tile by LDS-DMA: wave w's instruction j fills LDS slots
+  // 64 (w + 8 j) .. + 63 of the tile; slot p is position p % CPR of row
+  // p / CPR and takes chunk position ^ (row % CPR) of that key row.
+  constexpr int DJ = TILE * CPR / (kPfWaves * kWave);
+  static_assert(DJ * kPfWaves * kWave == TILE * CPR, "whole wave-loads per tile");
+  auto dma = [&](int tile, int buf) {
+    const int base = __builtin_amdgcn_readfirstlane(k0 + tile * TILE);
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+      const int slot = kWave * (wave + kPfWaves * j) + lane;
+      const int r = slot / CPR;
+      const int c = (slot % CPR) ^ (r & (CPR - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          kr, (__attribute__((address_space(3))) void*)(&ks[buf][kWave * 16 * (wave + kPfWaves * j)]),
+          16, (unsigned)((base + r) * ROWB + c * 16), 0, 0, 0);
+    }
+  };
+  if constexpr (kPipe) {
+    dma(0, 0);
+  } else {
+    gload(0);
+    lstore(0);
+  }
   // Every prologue load (query block, head weights) lands before the tile
   // loop.  Left in flight, the compiler's wait counts carry them into the
   // loop, where the first epilogue then waits vmcnt(3..0) on each pass: that
@@ -252,10 +276,13 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     constexpr int NS = TILE / 32;    // sub-blocks per tile
     static_assert(NS % 2 == 0, "a tile's last products land in the second accumulator");
     auto read_b = [&](int buf, int sb, i32x4(&bv)[NV]) {
-      const uint8_t* bp = &ks[buf][(sb * 32 + col) * PITCH + g * HALF];
+      const int r = sb * 32 + col;
+      const uint8_t* bp = &ks[buf][r * PITCH];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) bv[v] = *reinterpret_cast<const i32x4*>(bp + 16 * v);
+      for (int v = 0; v < NV; ++v)
+        bv[v] = *reinterpret_cast<const i32x4*>(bp + 16 * ((g * NV + v) ^ (r & (CPR - 1))));
     };
+
     auto prod = [&](int i, const i32x4(&bv)[NV], f32x16(&acc)[HB]) {
       const int s = i / HB, hb = i % HB;
       acc[hb] = mfma32_bf16(as_bf16x8(qv[hb][s]), as_bf16x8(bv[s]), s == 0 ? f32x16{} : acc[hb]);
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile & 1;
       const bool more = tile + 1 < ntiles;
-      if (more) gload(tile + 1);
+      if (more) dma(tile + 1, buf ^ 1);  // (every wave finished that buffer before the barrier)
       const int tbase = k0 + tile * TILE;
 #pragma unroll
       for (int sb = 0; sb + 1 < NS; ++sb) {
@@ -319,8 +346,13 @@ __global__ __launch_bounds__(kPfThreads, FP8 ? 4 : 2) void indexer_prefill_kerne
         overlap(tbase + 32 * sb, (sb & 1) ? acc1 : acc0, bv, (sb & 1) ? acc0 : acc1);
       }
       if (more) {
-        lstore(buf ^ 1);
-        __syncthreads();
+        // this wave's DMA of the next tile has landed (the memory counter
+        // completes in order: only the NS - 1 score stores since are left),
+        // then every wave's has
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (NS - 1));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         read_b(buf ^ 1, 0, bv);
         overlap(tbase + 32 * (NS - 1), acc1, bv, acc0);
       } else {
