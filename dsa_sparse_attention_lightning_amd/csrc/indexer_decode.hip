@@ -44,13 +44,13 @@
 // part of the row's histogram lies in a bin at or below that of the whole
 // row, and keys in bins at or above it are a superset of the true candidates
 // (the finishing pass never emits the extra ones).  Each wave hands its
-// eighth of the workgroup's bins to the row histogram three quarters of the
-// way through its tiles (an LDS exchange with zero, then device-scope adds);
+// eighth of the workgroup's bins to the row histogram half way through its
+// tiles (an LDS exchange with zero, then device-scope adds);
 // at the end a workgroup reads the row histogram as it stands, adds the
 // counts it has not handed off yet (they cannot be in what it read), takes
 // the threshold bin of that sum, and hands those counts off after the read
-// has returned.  So the bound covers about three quarters of every
-// workgroup's keys plus all of its own.
+// has returned.  So the bound covers about half of every workgroup's keys
+// (more for those that finished first) plus all of its own.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 2) void indexer_decode_kernel(
       first < wg_end ? min(tiles_per_wave, (wg_end - first + wstride - 1) / wstride) : 0;
   auto tmap = [&](int j) { return __builtin_amdgcn_readfirstlane(first + j * wstride); };
   // fused: the tile after which a wave hands its bins off (none if < 0)
-  const int hand_off = (3 * tend) / 4 - 1;
+  const int hand_off = tend / 2 - 1;
   int64_t pos = 0;  // the row's position: read after the first loads are issued
   unsigned char* my_stage = stage + wave * TK * PITCH;
 
