@@ -583,9 +583,10 @@ __global__ __launch_bounds__(NW * kWave) void sparse_mla_kernel(
   }
 }
 
-// Merge split-KV partials.  One workgroup per (query row, 2 heads); a thread
-// owns 8 dims.
-constexpr int kCombHeads = 2;
+// Merge split-KV partials.  One one-wave workgroup per (query row, head)
+// (measured against 2 and 4 heads per workgroup: 19.7-19.9 against
+// 19.8-20.1 us per layer with the main kernel); a thread owns 8 dims.
+constexpr int kCombHeads = 1;
 __global__ __launch_bounds__(kCombHeads * 64) void sparse_mla_combine_kernel(
     const __bf16* __restrict__ part_o, const float* __restrict__ part_lse, int Hq, int n_split,
     __bf16* __restrict__ out, float* __restrict__ lse) {
