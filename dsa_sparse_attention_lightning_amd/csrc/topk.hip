@@ -385,7 +385,7 @@ __device__ __forceinline__ void row_in_registers(__amdgpu_buffer_rsrc_t r, int n
   // and the counts above it are exact, otherwise (a sample that ran high)
   // every key is counted.  A row reaching this path has n > k; with fewer
   // than kSample valid sample keys the bound is bin 0 (every key).
-  constexpr uint32_t kSample = 128;
+  constexpr uint32_t kSample = 64;
   static_assert(kSample <= (uint32_t)kTkThreads, "one sample key per thread");
   const uint32_t valid = (uint32_t)min(kTkThreads, (n + 15) / 16);
   for (int i = tid; i < kBins1; i += kTkThreads) sm.hist[i] = 0;
