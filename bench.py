@@ -31,6 +31,7 @@ Also reported on the same line:
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
                 [--no-sweep] [--no-search] [--no-kv-append] [--search-only] [--kv-append-only]
+                [--stream-probe-only]
 """
 from __future__ import annotations
 
@@ -779,6 +780,43 @@ def kv_append_bench(dev, reps=200):
     return out
 
 
+
+def stream_probe_bench(dev, replays=8):
+    """Streaming-read ceiling for the decode indexer: a plain read of the bytes
+    one indexer launch moves at batch 8 x 131072 context (142,675,968, rounded
+    up to whole 8 KB tiles), in the indexer's own load pattern (256 workgroups
+    of eight waves, contiguous runs of 8 KB tiles, two tiles in flight per
+    wave) and in other launch shapes.  Twelve copies of the buffer are read in
+    turn (1.7 GB, far beyond the L2 and last-level caches), one graph replay
+    reading each copy once, so every read comes from HBM."""
+    import torch
+    import dsa_sparse_attention_lightning_amd as dsa
+    nbytes = (142675968 + 8191) // 8192 * 8192
+    copies = 12
+    bufs = [torch.full((nbytes,), c, dtype=torch.uint8, device=dev) for c in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {"bytes": nbytes, "copies": copies}
+    for name, form, wgs in (("tiles_256wg", "tiles", 256), ("tiles_512wg", "tiles", 512),
+                            ("tiles_1024wg", "tiles", 1024), ("stride_1024wg", "stride", 1024),
+                            ("stride_2048wg", "stride", 2048)):
+        for b in bufs:
+            dsa.probe_stream_read(b, sink, wgs, form)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for b in bufs:
+                dsa.probe_stream_read(b, sink, wgs, form)
+        ms = event_time_ms(lambda i=0: graph.replay(), replays, 1) / copies
+        del graph
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = dict(us=round(ms * 1e3, 2), gbs=round(gbs, 1),
+                         frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        log(f"stream read {name}: {ms * 1e3:.2f} us ({gbs:.0f} GB/s, "
+            f"{100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return out
+
 def environment():
     """Where the numbers were taken: GPU, gfx target, ROCm and torch versions,
     the GPU shader clock as rocm-smi reports it, host CPU model and threads."""
@@ -901,6 +939,10 @@ def main():
                     help="run only the pattern-search leg and print its JSON object")
     ap.add_argument("--kv-append-only", action="store_true",
                     help="run only the KV-cache append leg and print its JSON object")
+    ap.add_argument("--no-stream-probe", action="store_true",
+                    help="skip the streaming-read ceiling probe")
+    ap.add_argument("--stream-probe-only", action="store_true",
+                    help="run only the streaming-read ceiling probe and print its JSON object")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill legs (kernels and 4-layer stack) and print "
                          "their JSON object")
@@ -932,6 +974,9 @@ def main():
     if args.search_only:
         print(json.dumps({"pattern_search": pattern_search_bench(dev)}), flush=True)
         return
+    if args.stream_probe_only:
+        print(json.dumps({"stream_read_ceiling": stream_probe_bench(dev)}), flush=True)
+        return
     if args.kv_append_only:
         print(json.dumps({"kv_append": kv_append_bench(dev)}), flush=True)
         return
@@ -957,6 +1002,7 @@ def main():
     prefill = None if args.no_prefill else prefill_bench(dev, cpu=not args.no_cpu_baseline)
     prefill_stack = None if args.no_prefill else prefill_stack_bench(dev)
     kv_app = None if args.no_kv_append else kv_append_bench(dev)
+    ceiling = None if args.no_stream_probe else stream_probe_bench(dev)
     prefill_ctx = None
     if not (args.no_prefill or args.no_prefill_context):
         prefill_ctx = prefill_context_bench(dev)
@@ -997,6 +1043,7 @@ def main():
         "prefill_stack": prefill_stack,
         "prefill_context": prefill_ctx,
         "kv_append": kv_app,
+        "stream_read_ceiling": ceiling,
         "pattern_search": search,
         "pattern_sweep": sweep,
     }

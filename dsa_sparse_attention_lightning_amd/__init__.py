@@ -21,7 +21,7 @@ from typing import Dict, List, Optional, Sequence
 from . import _lib
 from ._lib import DSAError, Layer, StackShape, StackStats  # noqa: F401
 
-__all__ = ["indexer_scores", "topk", "topk_workspace_size", "indexer_topk",
+__all__ = ["probe_stream_read", "indexer_scores", "topk", "topk_workspace_size", "indexer_topk",
            "indexer_topk_workspace_size", "sparse_attn",
            "sparse_attn_workspace_size", "kv_append", "run_stack",
            "reuse_costs", "reuse_costs_workspace_size", "pattern_cost", "greedy_search",
@@ -306,6 +306,26 @@ def kv_append(ctx_len, kv_new=None, kv_cache=None, k_new=None, k_cache=None, k_s
                                        d_qk, D, dt, _ptr(kv_cache), _ptr(k_cache), _ptr(k_scale),
                                        _stream(stream)))
 
+
+
+def probe_stream_read(src, sink, workgroups: int = 256, form: str = "tiles", stream=None):
+    """Read every byte of the contiguous device tensor `src` once (a streaming-read
+    ceiling for the decode indexer's key sweep; no step of the method).
+
+    form "tiles": the indexer's load pattern, `workgroups` workgroups each sweeping
+    a contiguous run of 8 KB tiles; "stride": a grid-stride sweep. `sink` is a
+    device int32 tensor the kernel almost never writes. src.nbytes must be a
+    multiple of 8192."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise TypeError("src must be a contiguous device tensor")
+    _need(sink, "sink", (_torch().int32,))
+    _same_device(src, ("sink", sink))
+    forms = {"tiles": _lib.DSA_PROBE_TILES, "stride": _lib.DSA_PROBE_STRIDE}
+    if form not in forms:
+        raise ValueError(f"form must be one of {sorted(forms)}")
+    nbytes = src.numel() * src.element_size()
+    _lib.check(library().dsa_probe_stream_read(_ptr(src), nbytes, workgroups, forms[form],
+                                               _ptr(sink), _stream(stream)))
 
 def _layer_array(layers):
     arr = (Layer * len(layers))()

@@ -12,6 +12,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "dsa_indexcache.h")
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 DSA_BF16, DSA_FP8_E4M3 = 0, 1
 DSA_PROXY_OUTPUT, DSA_PROXY_MISS = 0, 1
+DSA_PROBE_TILES, DSA_PROBE_STRIDE = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 
@@ -54,6 +55,7 @@ SIGNATURES = {
                                 c_int, c_f32, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "dsa_kv_append": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_vp,
                               c_vp, c_vp, c_vp]),
+    "dsa_probe_stream_read": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_vp]),
     "indexcache_stack_workspace_size": (c_int, [ctypes.POINTER(StackShape), c_size_p]),
     "indexcache_stack_fuses_topk": (c_int, [ctypes.POINTER(StackShape),
                                             ctypes.POINTER(ctypes.c_int)]),

@@ -583,6 +583,27 @@ dsa_status_t dsa_kv_append(const float* kv_new, const float* k_new, const int32_
                     "kv append launch");
 }
 
+dsa_status_t dsa_probe_stream_read(const void* src, int64_t bytes, int workgroups, int form,
+                                   int32_t* sink, hipStream_t stream) {
+  const char* fn = "dsa_probe_stream_read";
+  CHECK_PTR(src);
+  CHECK_PTR(sink);
+  CHECK(bytes > 0 && bytes % 8192 == 0, DSA_ERR_INVALID_ARG,
+        "%s: bytes must be a positive multiple of 8192 (got %lld)", fn, (long long)bytes);
+  CHECK(workgroups >= 1 && workgroups <= 65536, DSA_ERR_INVALID_ARG,
+        "%s: workgroups must be in 1..65536 (got %d)", fn, workgroups);
+  CHECK(form == DSA_PROBE_TILES || form == DSA_PROBE_STRIDE, DSA_ERR_INVALID_ARG,
+        "%s: unknown form %d", fn, form);
+  const int64_t tiles = bytes / 8192;
+  // Tiles form: each workgroup's run is addressed through one 32-bit buffer range.
+  CHECK(form != DSA_PROBE_TILES || (tiles + workgroups - 1) / workgroups * 8192 <= kMaxSeqBytes,
+        DSA_ERR_UNSUPPORTED, "%s: %lld bytes over %d workgroups exceeds 2^31 - 1 per workgroup",
+        fn, (long long)bytes, workgroups);
+  return hip_status(dsa::launch_stream_probe(src, tiles, workgroups, form == DSA_PROBE_STRIDE,
+                                             sink, stream),
+                    "stream probe launch");
+}
+
 dsa_status_t indexcache_stack_workspace_size(const dsa_stack_shape_t* s, size_t* bytes) {
   const char* fn = "indexcache_stack_workspace_size";
   CHECK(s != nullptr && bytes != nullptr, DSA_ERR_INVALID_ARG, "%s: NULL argument", fn);

@@ -102,6 +102,12 @@ hipError_t launch_kv_append(const float* kv_new, const float* k_new, const int32
                             int B, int T, int Lmax, int d_qk, int D, bool k_fp8, void* kv_cache,
                             void* k_cache, float* k_scale, hipStream_t stream);
 
+// Streaming-read probe: reads tiles * 8192 bytes at src once (tiles form:
+// the decode indexer's sweep over `workgroups` contiguous runs; stride form:
+// a grid-stride sweep).  Writes *sink only on a one-in-2^32 fold value.
+hipError_t launch_stream_probe(const void* src, int64_t tiles, int workgroups, bool stride_form,
+                               int32_t* sink, hipStream_t stream);
+
 // Pattern-search proxy costs.  Each writes one fp64 value to *dst (device)
 // after a reduction whose per-workgroup partials go to `partials`, which
 // must hold kReuseCostMaxGrid entries.

@@ -204,6 +204,30 @@ dsa_status_t dsa_kv_append(const float* kv_new, const float* k_new, const int32_
                            int B, int T, int Lmax, int d_qk, int D, dsa_dtype_t k_dtype,
                            void* kv_cache, void* k_cache, float* k_scale, hipStream_t stream);
 
+/* Streaming-read probe: a measurement aid, not a step of the method.  For
+ * benchmarks that compare the decode indexer's key sweep with a plain read of
+ * the same number of bytes, i.e. the practical HBM ceiling of that sweep.
+ * Reads `bytes` bytes of device memory at `src` once and keeps nothing:
+ *   DSA_PROBE_TILES  - the indexer's own load pattern: `workgroups`
+ *                      workgroups of eight waves, each owning a contiguous
+ *                      run of 8 KB tiles that its waves take interleaved,
+ *                      two tiles (16 KB) in flight per wave;
+ *   DSA_PROBE_STRIDE - a grid-stride sweep by `workgroups` workgroups of
+ *                      512 threads, eight 16-byte loads in flight per lane.
+ * All loads are 16-byte non-temporal loads.  The loaded words are folded by
+ * XOR and a lane writes its fold to *sink only when it equals one fixed
+ * 32-bit value, so *sink (device int32, caller-owned) is almost never
+ * written and its contents mean nothing.
+ * src: device, 16-byte aligned, `bytes` a positive multiple of 8192;
+ * workgroups in 1..65536; in the tiles form each workgroup's run must stay
+ * below 2^31 bytes.  Violations return DSA_ERR_INVALID_ARG or
+ * DSA_ERR_UNSUPPORTED before any launch.
+ */
+#define DSA_PROBE_TILES 0
+#define DSA_PROBE_STRIDE 1
+dsa_status_t dsa_probe_stream_read(const void* src, int64_t bytes, int workgroups, int form,
+                                   int32_t* sink, hipStream_t stream);
+
 /* One layer's device tensors for indexcache_run_stack.  q_idx / w / k_idx
  * (and the fp8 scales) are read on F layers only; q / kv / out (and lse)
  * only when shape->Hq > 0. */

@@ -167,6 +167,26 @@ def test_kv_append_rejects_bad_arguments(lib):
     assert "aligned" in _err(lib)
 
 
+
+def test_stream_probe_rejects_bad_arguments(lib):
+    f = lib.dsa_probe_stream_read
+    # (src, bytes, workgroups, form, sink, stream)
+    assert f(None, 8192, 256, 0, 16, None) == 1
+    assert "src is NULL" in _err(lib)
+    assert f(16, 8192, 256, 0, None, None) == 1
+    assert "sink is NULL" in _err(lib)
+    assert f(16, 8000, 256, 0, 16, None) == 1              # not whole 8 KB tiles
+    assert "multiple of 8192" in _err(lib)
+    assert f(16, 0, 256, 0, 16, None) == 1
+    assert f(16, 8192, 0, 0, 16, None) == 1                # no workgroups
+    assert f(16, 8192, 65537, 1, 16, None) == 1
+    assert f(16, 8192, 256, 2, 16, None) == 1              # unknown form
+    assert "form" in _err(lib)
+    assert f(24, 8192, 256, 0, 16, None) == 1              # misaligned
+    assert "aligned" in _err(lib)
+    assert f(16, 1 << 32, 1, 0, 16, None) == 2             # one run of 4 GiB
+    assert "2^31" in _err(lib)
+
 C_PROGRAM = r"""
 #include <stdio.h>
 #include <string.h>
