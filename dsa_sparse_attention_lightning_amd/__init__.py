@@ -319,6 +319,8 @@ def probe_stream_read(src, sink, workgroups: int = 256, form: str = "tiles", str
     if not src.is_cuda or not src.is_contiguous():
         raise TypeError("src must be a contiguous device tensor")
     _need(sink, "sink", (_torch().int32,))
+    if sink.numel() < 1:
+        raise TypeError("sink must hold at least one int32")
     _same_device(src, ("sink", sink))
     forms = {"tiles": _lib.DSA_PROBE_TILES, "stride": _lib.DSA_PROBE_STRIDE}
     if form not in forms:
